@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark: one layer of SIFT bit-vector sparse RAG prefill on one MI355X.
+
+A step is the whole hot path for one layer over the Llama-3.1-8B attention
+shape with 10 retrieved documents of 1024 tokens and a 128-token question
+(32 q / 8 kv heads, head_dim 128, bf16, LA density 25 %, CA density 20 %):
+  sift_decode_bits    (LA/CA bits -> CSR of KV tiles)
+  sift_sparse_prefill (block-sparse causal GQA attention over the CSR)
+with every input already resident in HBM.  Prints one JSON line.
+
+value = effective TFLOP/s of the step: computed tiles x 4 * 64 * 64 * D FLOP
+(QK^T and PV, diagonal tiles counted whole, skipped tiles never counted)
+divided by the step time.  The roofline block reports the attention kernel
+alone against the bf16 dense MFMA peak, timed with HIP events on the stream it
+runs on.  The CPU baseline is the fp64 oracle on a bounded sample of rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "ms/layer and effective TFLOP/s (% bf16 MFMA peak) of bit-vector sparse prefill"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+WORKLOADS = {
+    1: "tiny: 1 q / 1 kv head, D 64, fp32 in, 2 docs x 256 + 64-token question (576 tokens)",
+    2: "llama3.1-8b attention layer: 32 q / 8 kv heads, D 128, bf16, 10 docs x 1024 + "
+       "128-token question (10368 tokens), LA 25% / CA 20% Bernoulli, diagonal and page 0 on",
+    3: "llama3.1-8b at 32K: 32 q / 8 kv heads, D 128, bf16, 32 docs x 1024 + 256-token question "
+       "(33024 tokens), LA 15% / CA 10%",
+    4: "qwen3-235b-a22b attention layer: 64 q / 4 kv heads, D 128, bf16, 20 docs x 2048 + "
+       "256-token question (41216 tokens), LA 12% / CA 8%",
+    5: "ragged batch: 4 requests of 16-40 docs (300-3000 tokens) + 64-512-token question, "
+       "32 q / 8 kv heads, D 128, bf16, Beta(2,8) per-head densities",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(case, row_ptr, target_seconds, seed=0):
+    """Time the fp64 oracle on whole CSR rows until about target_seconds of work."""
+    import oracle
+
+    G = case.q.shape[0] // 64
+    D = case.head_dim
+    rows_total = case.num_q_heads * G
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(rows_total)
+    per_tile = 4.0 * 64 * 64 * D
+
+    def run(rows):
+        heads = np.repeat(rows // G, 64).astype(np.int32)
+        toks = (np.repeat(rows % G, 64) * 64 + np.tile(np.arange(64), rows.size)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attention(case, heads=heads, tokens=toks)
+        return time.perf_counter() - t0, float(sum(int(row_ptr[r + 1] - row_ptr[r]) for r in rows)) * per_tile
+
+    calib = order[:8]
+    dt, fl = run(calib)
+    rate = fl / max(dt, 1e-9)
+    # choose rows until the expected work reaches the target
+    lens = np.array([int(row_ptr[r + 1] - row_ptr[r]) for r in order], dtype=np.float64) * per_tile
+    budget = rate * target_seconds
+    n = int(np.searchsorted(np.cumsum(lens[8:]), budget)) + 1
+    sample = order[8: 8 + max(n, 1)]
+    dt, fl = run(sample)
+    total_fl = float(np.sum(lens))
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(oracle.max_threads()),
+        "kind": "oracle",
+        "sample": (f"{sample.size} of {rows_total} (head, query-tile) rows, "
+                   f"{100.0 * fl / total_fl:.1f}% of the layer's computed tiles, {dt:.1f} s wall"),
+        "seconds": dt,
+        "ms_per_layer_extrapolated": dt * total_fl / fl * 1e3,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS),
+                    help="synthetic workload id (2 = the Llama-3.1-8B 10 x 1K layer)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU work budget of the oracle baseline (0 disables it)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is by q-head groups or by request, see the design notes); run with --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import bit_vector_block_amd as sift
+    from bit_vector_block_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating workload {args.workload}")
+    case = W.config_case(args.workload)
+    lay = sift.Layout.from_case(case)
+    N, Hq, Hkv, D = lay.padded_tokens, case.num_q_heads, case.num_kv_heads, case.head_dim
+
+    def to_dev_words(w):
+        w = np.ascontiguousarray(w, dtype=np.uint32)
+        return torch.from_numpy((w if w.size else np.zeros(1, np.uint32)).view(np.int32)).to(dev)
+
+    def to_dev_vals(x):
+        if case.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+    la, ca = to_dev_words(case.la_words), to_dev_words(case.ca_words)
+    q, k, v = (to_dev_vals(x) for x in (case.q, case.k, case.v))
+    plan = sift.plan_upload(lay, dev)
+    row_ptr = torch.empty(lay.num_rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(lay.csr_max_nnz, 1), dtype=torch.int32, device=dev)
+    dt_code = sift.SIFT_BF16 if case.dtype == "bf16" else sift.SIFT_FP32
+    ws = torch.empty(max(lay.workspace_bytes(dt_code), 1), dtype=torch.uint8, device=dev)
+    out = torch.empty((N, Hq, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sift.decode_bits(lay, la, ca, plan=plan, workspace=ws, row_ptr=row_ptr, col_idx=col_idx)
+        if ev is not None:
+            ev[1].record(stream)
+        sift.sparse_prefill(lay, q, k, v, row_ptr, col_idx, plan=plan, workspace=ws, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    rp_host = row_ptr.cpu().numpy().astype(np.int64)
+    nnz = int(rp_host[-1])
+
+    log(f"timing {args.steps} steps")
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    decode_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    prefill_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    flops = float(nnz) * 4.0 * 64 * 64 * D
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (prefill_ms * 1e-3) / 1e12
+    decode_bytes = 4.0 * (lay.la_words + lay.ca_words + lay.num_rows + 1 + nnz)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V and Bernoulli LA/CA bits; no dataset or weights)",
+        "config": {
+            "workload": WORKLOADS[args.workload],
+            "tokens_padded": N,
+            "q_heads": Hq,
+            "kv_heads": Hkv,
+            "head_dim": D,
+            "csr_rows": lay.num_rows,
+            "computed_tiles": nnz,
+            "effective_gflop_per_layer": round(flops / 1e9, 3),
+        },
+        "ms_per_layer": round(ms_per_step, 5),
+        "decode_us": round(decode_ms * 1e3, 2),
+        "decode_gbs": round(decode_bytes / (decode_ms * 1e-3) / 1e9, 1),
+        "prefill_ms": round(prefill_ms, 5),
+        "pct_bf16_peak_step": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "kernel": f"sparse_prefill_kernel<{D}>",
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if args.cpu_seconds > 0:
+        log(f"cpu baseline (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(case, rp_host, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

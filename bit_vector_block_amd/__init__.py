@@ -1,0 +1,14 @@
+"""bit_vector_block_amd: SIFT bit-vector sparse RAG prefill on MI355X (gfx950).
+
+Two hand-written HIP kernels behind the C ABI of include/sift.h:
+  * ``decode_bits``    -- LA/CA bit vectors -> per-(head, query tile) CSR of KV tiles;
+  * ``sparse_prefill`` -- block-sparse causal GQA attention over that CSR
+                          (bf16 MFMA, online softmax, fp32 output).
+This package is the ctypes binding (argument marshalling) plus the seeded
+synthetic workloads in ``workloads``.
+"""
+from ._binding import (SIFT_BF16, SIFT_FP32, Layout, SiftError, decode_bits, default_scale,
+                       library, plan_upload, sparse_prefill)
+
+__all__ = ["Layout", "SiftError", "decode_bits", "sparse_prefill", "plan_upload", "library",
+           "default_scale", "SIFT_BF16", "SIFT_FP32"]

@@ -1,0 +1,327 @@
+// Host side of libsift.so: layout validation, sizing, the device plan, and the
+// extern "C" entry points declared in include/sift.h.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "sift_internal.hpp"
+
+namespace sift {
+
+namespace {
+
+constexpr int32_t kPlanVersion = 1;
+constexpr int64_t kInt32Max = 2147483647LL;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+uint64_t fnv1a(uint64_t h, const void *data, size_t n) {
+    const unsigned char *p = static_cast<const unsigned char *>(data);
+    for (size_t i = 0; i < n; ++i) {
+        h ^= p[i];
+        h *= 1099511628211ULL;
+    }
+    return h;
+}
+
+}  // namespace
+
+sift_status build_layout(const sift_layout *layout, HostLayout *out) {
+    if (!layout || !out) return SIFT_ERR_INVALID;
+    const sift_layout &L = *layout;
+    if (L.num_requests < 1 || !L.req_num_docs || !L.question_len) return SIFT_ERR_INVALID;
+    if (L.num_q_heads < 1 || L.num_kv_heads < 1 || L.num_q_heads % L.num_kv_heads != 0)
+        return SIFT_ERR_INVALID;
+    int64_t ndocs = 0;
+    for (int32_t b = 0; b < L.num_requests; ++b) {
+        if (L.req_num_docs[b] < 0 || L.question_len[b] < 0) return SIFT_ERR_INVALID;
+        ndocs += L.req_num_docs[b];
+    }
+    if (ndocs > 0 && !L.doc_len) return SIFT_ERR_INVALID;
+    if (L.tile != kTile) return SIFT_ERR_UNSUPPORTED;
+    if (L.head_dim != 64 && L.head_dim != 128) return SIFT_ERR_UNSUPPORTED;
+    if (ndocs > kInt32Max) return SIFT_ERR_UNSUPPORTED;
+
+    HostLayout hl;
+    hl.R = L.num_requests;
+    hl.ndocs = static_cast<int32_t>(ndocs);
+    hl.Hq = L.num_q_heads;
+    hl.Hkv = L.num_kv_heads;
+    hl.D = L.head_dim;
+
+    int64_t G = 0, la_words = 0, ca_words = 0, max_nnz = 0;
+    for (int64_t d = 0; d < ndocs; ++d)
+        if (L.doc_len[d] < 1) return SIFT_ERR_INVALID;
+    {
+        int64_t d = 0;
+        for (int32_t b = 0; b < L.num_requests; ++b) {
+            int64_t tb = 0;
+            for (int32_t i = 0; i < L.req_num_docs[b]; ++i, ++d) {
+                const int64_t T = ceil_div(L.doc_len[d], kTile);
+                tb += T;
+                la_words += static_cast<int64_t>(L.num_q_heads) * ceil_div(T * (T + 1) / 2, 32);
+                ca_words += static_cast<int64_t>(L.num_q_heads) * ceil_div(T, 32);
+            }
+            tb += ceil_div(L.question_len[b], kTile);
+            G += tb;
+            max_nnz += tb * (tb + 1) / 2;
+        }
+    }
+    max_nnz *= L.num_q_heads;
+    // Token indices, CSR entries and word offsets are int32 on the device.
+    if (G * kTile > kInt32Max || G * L.num_q_heads >= kInt32Max || max_nnz >= kInt32Max ||
+        la_words > kInt32Max || ca_words > kInt32Max)
+        return SIFT_ERR_UNSUPPORTED;
+    hl.G = static_cast<int32_t>(G);
+    hl.la_words = la_words;
+    hl.ca_words = ca_words;
+    hl.max_nnz = max_nnz;
+
+    uint64_t fp = 1469598103934665603ULL;
+    const int32_t dims[4] = {L.num_requests, L.num_q_heads, L.num_kv_heads, L.head_dim};
+    fp = fnv1a(fp, dims, sizeof(dims));
+    fp = fnv1a(fp, L.req_num_docs, sizeof(int32_t) * L.num_requests);
+    fp = fnv1a(fp, L.question_len, sizeof(int32_t) * L.num_requests);
+    if (ndocs) fp = fnv1a(fp, L.doc_len, sizeof(int32_t) * ndocs);
+    hl.fingerprint = fp;
+
+    // plan image
+    const int64_t nd = ndocs, R = L.num_requests;
+    std::vector<int32_t> &p = hl.plan;
+    p.assign(kHeaderWords + 3 * G + 7 * nd + 3 * R, 0);
+    int32_t *hdr = p.data();
+    hdr[0] = static_cast<int32_t>(kPlanMagic);
+    hdr[1] = kPlanVersion;
+    hdr[2] = static_cast<int32_t>(fp & 0xffffffffu);
+    hdr[3] = static_cast<int32_t>(fp >> 32);
+    hdr[4] = L.num_requests;
+    hdr[5] = hl.ndocs;
+    hdr[6] = hl.G;
+    hdr[7] = hl.Hq;
+    int32_t *tile_doc = hdr + kHeaderWords;
+    int32_t *tile_local = tile_doc + G;
+    int32_t *tile_valid = tile_local + G;
+    int32_t *doc_first = tile_valid + G;
+    int32_t *doc_tiles = doc_first + nd;
+    int32_t *doc_la_off = doc_tiles + nd;
+    int32_t *doc_ca_off = doc_la_off + nd;
+    int32_t *doc_la_w = doc_ca_off + nd;
+    int32_t *doc_ca_w = doc_la_w + nd;
+    int32_t *doc_req = doc_ca_w + nd;
+    int32_t *req_first = doc_req + nd;
+    int32_t *req_first_doc = req_first + R;
+    int32_t *req_ndocs = req_first_doc + R;
+    int64_t g = 0, d = 0, la_acc = 0, ca_acc = 0;
+    for (int32_t b = 0; b < L.num_requests; ++b) {
+        req_first[b] = static_cast<int32_t>(g);
+        req_first_doc[b] = static_cast<int32_t>(d);
+        req_ndocs[b] = L.req_num_docs[b];
+        for (int32_t i = 0; i < L.req_num_docs[b]; ++i, ++d) {
+            const int64_t n = L.doc_len[d];
+            const int64_t T = ceil_div(n, kTile);
+            doc_first[d] = static_cast<int32_t>(g);
+            doc_req[d] = b;
+            doc_tiles[d] = static_cast<int32_t>(T);
+            doc_la_w[d] = static_cast<int32_t>(ceil_div(T * (T + 1) / 2, 32));
+            doc_ca_w[d] = static_cast<int32_t>(ceil_div(T, 32));
+            doc_la_off[d] = static_cast<int32_t>(la_acc);
+            doc_ca_off[d] = static_cast<int32_t>(ca_acc);
+            la_acc += static_cast<int64_t>(L.num_q_heads) * doc_la_w[d];
+            ca_acc += static_cast<int64_t>(L.num_q_heads) * doc_ca_w[d];
+            for (int64_t r = 0; r < T; ++r, ++g) {
+                tile_doc[g] = static_cast<int32_t>(d);
+                tile_local[g] = static_cast<int32_t>(r);
+                tile_valid[g] = static_cast<int32_t>(std::min<int64_t>(kTile, n - r * kTile));
+            }
+        }
+        const int64_t m = L.question_len[b];
+        const int64_t TQ = ceil_div(m, kTile);
+        for (int64_t r = 0; r < TQ; ++r, ++g) {
+            tile_doc[g] = -(b + 1);
+            tile_local[g] = static_cast<int32_t>(r);
+            tile_valid[g] = static_cast<int32_t>(std::min<int64_t>(kTile, m - r * kTile));
+        }
+    }
+    *out = std::move(hl);
+    return SIFT_OK;
+}
+
+PlanView plan_view(const HostLayout &hl, const void *d_plan) {
+    const int32_t *base = static_cast<const int32_t *>(d_plan);
+    const int64_t G = hl.G, nd = hl.ndocs, R = hl.R;
+    PlanView v;
+    v.header = base;
+    v.tile_doc = base + kHeaderWords;
+    v.tile_local = v.tile_doc + G;
+    v.tile_valid = v.tile_local + G;
+    v.doc_first = v.tile_valid + G;
+    v.doc_tiles = v.doc_first + nd;
+    v.doc_la_off = v.doc_tiles + nd;
+    v.doc_ca_off = v.doc_la_off + nd;
+    v.doc_la_w = v.doc_ca_off + nd;
+    v.doc_ca_w = v.doc_la_w + nd;
+    v.doc_req = v.doc_ca_w + nd;
+    v.req_first = v.doc_req + nd;
+    v.req_first_doc = v.req_first + R;
+    v.req_ndocs = v.req_first_doc + R;
+    v.fp_lo = static_cast<uint32_t>(hl.fingerprint & 0xffffffffu);
+    v.fp_hi = static_cast<uint32_t>(hl.fingerprint >> 32);
+    v.num_requests = hl.R;
+    v.num_docs = hl.ndocs;
+    v.num_tiles = hl.G;
+    v.num_q_heads = hl.Hq;
+    return v;
+}
+
+// Decode scratch: ca_prefix [Hq][ndocs], row_local [Hq][G], head_total [Hq].
+size_t decode_workspace_bytes(const HostLayout &hl) {
+    return align256(sizeof(int32_t) * size_t(hl.Hq) * size_t(std::max(hl.ndocs, 1))) +
+           align256(sizeof(int32_t) * size_t(hl.Hq) * size_t(std::max(hl.G, 1))) +
+           align256(sizeof(int32_t) * size_t(hl.Hq));
+}
+
+static size_t prefill_workspace_bytes(const HostLayout &hl, sift_dtype dtype) {
+    if (dtype != SIFT_FP32) return 0;
+    const size_t N = size_t(hl.G) * kTile;
+    return align256(2 * N * hl.Hq * hl.D) + 2 * align256(2 * N * hl.Hkv * hl.D);
+}
+
+}  // namespace sift
+
+using namespace sift;
+
+extern "C" {
+
+int32_t sift_abi_version(void) { return (1 << 16) | 0; }
+
+const char *sift_status_string(sift_status s) {
+    switch (s) {
+        case SIFT_OK: return "SIFT_OK";
+        case SIFT_ERR_INVALID: return "SIFT_ERR_INVALID: invalid argument or layout";
+        case SIFT_ERR_CAPACITY: return "SIFT_ERR_CAPACITY: a caller buffer is too small";
+        case SIFT_ERR_UNSUPPORTED: return "SIFT_ERR_UNSUPPORTED: head_dim/tile unsupported or int32 overflow";
+        case SIFT_ERR_HIP: return "SIFT_ERR_HIP: HIP runtime or launch failure";
+    }
+    return "unknown sift_status";
+}
+
+int64_t sift_num_tiles(const sift_layout *layout) {
+    HostLayout hl;
+    return build_layout(layout, &hl) == SIFT_OK ? hl.G : -1;
+}
+
+int64_t sift_padded_tokens(const sift_layout *layout) {
+    HostLayout hl;
+    return build_layout(layout, &hl) == SIFT_OK ? int64_t(hl.G) * kTile : -1;
+}
+
+int64_t sift_num_rows(const sift_layout *layout) {
+    HostLayout hl;
+    return build_layout(layout, &hl) == SIFT_OK ? int64_t(hl.G) * hl.Hq : -1;
+}
+
+int64_t sift_la_words(const sift_layout *layout) {
+    HostLayout hl;
+    return build_layout(layout, &hl) == SIFT_OK ? hl.la_words : -1;
+}
+
+int64_t sift_ca_words(const sift_layout *layout) {
+    HostLayout hl;
+    return build_layout(layout, &hl) == SIFT_OK ? hl.ca_words : -1;
+}
+
+int64_t sift_csr_max_nnz(const sift_layout *layout) {
+    HostLayout hl;
+    return build_layout(layout, &hl) == SIFT_OK ? hl.max_nnz : -1;
+}
+
+size_t sift_plan_bytes(const sift_layout *layout) {
+    HostLayout hl;
+    return build_layout(layout, &hl) == SIFT_OK ? hl.plan.size() * sizeof(int32_t) : 0;
+}
+
+size_t sift_workspace_bytes(const sift_layout *layout, sift_dtype dtype) {
+    HostLayout hl;
+    if (build_layout(layout, &hl) != SIFT_OK) return 0;
+    if (dtype != SIFT_BF16 && dtype != SIFT_FP32) return 0;
+    return std::max(decode_workspace_bytes(hl), prefill_workspace_bytes(hl, dtype));
+}
+
+sift_status sift_plan_upload(const sift_layout *layout, void *d_plan, size_t plan_bytes,
+                             hipStream_t stream) {
+    HostLayout hl;
+    sift_status st = build_layout(layout, &hl);
+    if (st != SIFT_OK) return st;
+    if (!d_plan) return SIFT_ERR_INVALID;
+    const size_t need = hl.plan.size() * sizeof(int32_t);
+    if (plan_bytes < need) return SIFT_ERR_CAPACITY;
+    // Pageable source: the runtime stages it before returning, so the host
+    // vector may die right after the call.
+    if (hipMemcpyAsync(d_plan, hl.plan.data(), need, hipMemcpyHostToDevice, stream) != hipSuccess)
+        return SIFT_ERR_HIP;
+    return SIFT_OK;
+}
+
+sift_status sift_decode_bits(const sift_layout *layout, const void *d_plan, const uint32_t *d_la,
+                             const uint32_t *d_ca, int32_t *d_row_ptr, int32_t *d_col_idx,
+                             int64_t col_capacity, void *d_workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    HostLayout hl;
+    sift_status st = build_layout(layout, &hl);
+    if (st != SIFT_OK) return st;
+    if (!d_plan || !d_row_ptr) return SIFT_ERR_INVALID;
+    if ((hl.la_words > 0 && !d_la) || (hl.ca_words > 0 && !d_ca)) return SIFT_ERR_INVALID;
+    if (hl.max_nnz > 0 && !d_col_idx) return SIFT_ERR_INVALID;
+    if (col_capacity < hl.max_nnz) return SIFT_ERR_CAPACITY;
+    if (!d_workspace || workspace_bytes < decode_workspace_bytes(hl)) return SIFT_ERR_CAPACITY;
+    const PlanView pv = plan_view(hl, d_plan);
+    if (launch_decode(hl, pv, d_la, d_ca, d_row_ptr, d_col_idx, d_workspace, stream) != hipSuccess)
+        return SIFT_ERR_HIP;
+    return SIFT_OK;
+}
+
+sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan, const void *d_q,
+                                const void *d_k, const void *d_v, sift_dtype dtype,
+                                const int32_t *d_row_ptr, const int32_t *d_col_idx, float scale,
+                                float *d_out, float *d_lse, void *d_workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    HostLayout hl;
+    sift_status st = build_layout(layout, &hl);
+    if (st != SIFT_OK) return st;
+    if (dtype != SIFT_BF16 && dtype != SIFT_FP32) return SIFT_ERR_INVALID;
+    if (hl.G == 0) return SIFT_OK;
+    if (!d_plan || !d_q || !d_k || !d_v || !d_row_ptr || !d_col_idx || !d_out)
+        return SIFT_ERR_INVALID;
+    if (!(scale > 0.0f)) scale = 1.0f / sqrtf(float(hl.D));
+    if (!isfinite(scale)) return SIFT_ERR_INVALID;
+    const size_t need = prefill_workspace_bytes(hl, dtype);
+    if (need > 0 && (!d_workspace || workspace_bytes < need)) return SIFT_ERR_CAPACITY;
+    const PlanView pv = plan_view(hl, d_plan);
+    const uint16_t *q = static_cast<const uint16_t *>(d_q);
+    const uint16_t *k = static_cast<const uint16_t *>(d_k);
+    const uint16_t *v = static_cast<const uint16_t *>(d_v);
+    if (dtype == SIFT_FP32) {
+        const int64_t N = int64_t(hl.G) * kTile;
+        const int64_t nq = N * hl.Hq * hl.D, nkv = N * hl.Hkv * hl.D;
+        char *ws = static_cast<char *>(d_workspace);
+        uint16_t *qb = reinterpret_cast<uint16_t *>(ws);
+        uint16_t *kb = reinterpret_cast<uint16_t *>(ws + align256(2 * size_t(nq)));
+        uint16_t *vb = reinterpret_cast<uint16_t *>(ws + align256(2 * size_t(nq)) + align256(2 * size_t(nkv)));
+        if (launch_cast_bf16(static_cast<const float *>(d_q), qb, nq, stream) != hipSuccess ||
+            launch_cast_bf16(static_cast<const float *>(d_k), kb, nkv, stream) != hipSuccess ||
+            launch_cast_bf16(static_cast<const float *>(d_v), vb, nkv, stream) != hipSuccess)
+            return SIFT_ERR_HIP;
+        q = qb;
+        k = kb;
+        v = vb;
+    }
+    if (launch_prefill(hl, pv, q, k, v, d_row_ptr, d_col_idx, scale, d_out, d_lse, stream) !=
+        hipSuccess)
+        return SIFT_ERR_HIP;
+    return SIFT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Internal declarations shared by the libsift.so translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "sift.h"
+
+namespace sift {
+
+constexpr int kTile = 64;
+constexpr uint32_t kPlanMagic = 0x54464953u;  // "SIFT"
+constexpr int kHeaderWords = 16;
+
+// Device view of an uploaded plan.  Every array lives inside the plan buffer.
+struct PlanView {
+    const int32_t *header;      // [16]: magic, version, fp_lo, fp_hi, R, Ndocs, G, Hq, ...
+    const int32_t *tile_doc;    // [G]: global doc of a document tile, -(request+1) for a question tile
+    const int32_t *tile_local;  // [G]: tile index inside its segment
+    const int32_t *tile_valid;  // [G]: valid tokens in the tile (1..64)
+    const int32_t *doc_first;   // [Ndocs]: global first tile
+    const int32_t *doc_tiles;   // [Ndocs]: T_d
+    const int32_t *doc_la_off;  // [Ndocs]: word offset of the (d, head 0) LA vector
+    const int32_t *doc_ca_off;  // [Ndocs]
+    const int32_t *doc_la_w;    // [Ndocs]: words per (d, h) LA vector
+    const int32_t *doc_ca_w;    // [Ndocs]
+    const int32_t *doc_req;     // [Ndocs]: request of the document
+    const int32_t *req_first;   // [R]: global first tile of the request
+    const int32_t *req_first_doc;  // [R]: global index of the request's first document
+    const int32_t *req_ndocs;   // [R]
+    uint32_t fp_lo, fp_hi;      // fingerprint the host expects
+    int32_t num_requests, num_docs, num_tiles, num_q_heads;
+};
+
+// Host-side summary of a validated layout.
+struct HostLayout {
+    int32_t R = 0, ndocs = 0, G = 0, Hq = 0, Hkv = 0, D = 0;
+    int64_t la_words = 0, ca_words = 0, max_nnz = 0;
+    uint64_t fingerprint = 0;
+    std::vector<int32_t> plan;  // the full plan image (header + arrays)
+};
+
+// Validates `layout` and fills `out` (plan image included).  Returns SIFT_OK,
+// SIFT_ERR_INVALID or SIFT_ERR_UNSUPPORTED.
+sift_status build_layout(const sift_layout *layout, HostLayout *out);
+
+// Pointers into a device plan buffer laid out like HostLayout::plan.
+PlanView plan_view(const HostLayout &hl, const void *d_plan);
+
+size_t decode_workspace_bytes(const HostLayout &hl);
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_decode(const HostLayout &hl, const PlanView &pv, const uint32_t *la,
+                         const uint32_t *ca, int32_t *row_ptr, int32_t *col_idx, void *workspace,
+                         hipStream_t stream);
+hipError_t launch_cast_bf16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);
+hipError_t launch_prefill(const HostLayout &hl, const PlanView &pv, const uint16_t *q,
+                          const uint16_t *k, const uint16_t *v, const int32_t *row_ptr,
+                          const int32_t *col_idx, float scale, float *out, float *lse,
+                          hipStream_t stream);
+
+}  // namespace sift

@@ -223,6 +223,32 @@ def _ragged_case(cid=5, num_requests=4, max_request_tokens=65536):
                      hq, hkv, d, la_p, ca_p, "bf16", rng=rng)
 
 
+def config_layout(cid: int):
+    """(req_num_docs, doc_len, question_len, Hq, Hkv, D) of a workload, without drawing values."""
+    if cid == 5:
+        rng = np.random.default_rng(cid - 1)
+        req_num_docs, doc_len, question_len = [], [], []
+        for _ in range(4):
+            k = int(rng.integers(16, 41))
+            m = int(rng.integers(64, 513))
+            lens = rng.integers(300, 3001, size=k)
+            total = TILE * tiles_of(m)
+            kept = []
+            for n_d in lens:
+                if total + TILE * tiles_of(int(n_d)) > 65536:
+                    break
+                total += TILE * tiles_of(int(n_d))
+                kept.append(int(n_d))
+            req_num_docs.append(len(kept))
+            doc_len.extend(kept)
+            question_len.append(m)
+        return req_num_docs, doc_len, question_len, 32, 8, 128
+    shapes = {1: (2, 256, 64, 1, 1, 64), 2: (10, 1024, 128, 32, 8, 128),
+              3: (32, 1024, 256, 32, 8, 128), 4: (20, 2048, 256, 64, 4, 128)}
+    nd, n, m, hq, hkv, d = shapes[cid]
+    return [nd], [n] * nd, [m], hq, hkv, d
+
+
 def config_case(cid: int) -> Case:
     """The five workloads (1 = tiny ... 5 = ragged batch); seed = id - 1."""
     if cid == 1:

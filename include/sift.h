@@ -1,0 +1,169 @@
+/*
+ * sift.h -- C ABI of libsift.so: bit-vector sparse RAG prefill on MI355X (gfx950).
+ *
+ * SIFT (Selective-Index For Fast Compute of RAG Prefill by Exploiting Attention
+ * Invariance), technical summary, section 2 "Metodologia":
+ *   - "Design del Sistema": for every retrieved document, and per layer and
+ *     head, two compact bit vectors are stored.  Local-Attention (LA) bits mark
+ *     the high-score tiles of the document's own self-attention matrix;
+ *     Cross-Attention (CA) bits mark the document's KV pages (columns) that
+ *     draw attention from other documents.  At prefill time a sparse attention
+ *     kernel reads the bits and evaluates scores only on the marked tiles/pages.
+ *   - "Dettagli di Implementazione": a decode kernel turns the bit vectors into
+ *     explicit tile indices, and a FlashAttention-style kernel iterates over
+ *     those indices only.
+ *
+ * Readings fixed here where the pages are silent: tile = KV page = 64 tokens;
+ * CA pages of document i are visited by every query tile of every later
+ * document of the same request; question tokens attend densely and causally to
+ * every earlier token of their request; causality is per token.
+ *
+ * Data formats
+ * ------------
+ * Token layout: requests in order; in each request its documents in order and
+ * then its question; each segment is padded up to a multiple of 64 tokens.
+ * G = total tiles, N = 64 * G padded tokens.  Global tile g covers tokens
+ * [64 g, 64 g + 64).
+ *
+ * Q is [N][Hq][D], K and V are [N][Hkv][D], row-major, bf16 (or fp32, see
+ * sift_dtype), post-RoPE.  Padded slots may hold any finite values (padded
+ * K slots may even hold NaN); they are never attended.  Query head h reads
+ * KV head h / (Hq / Hkv).
+ *
+ * Bits (one layer): LA(d,h; r,c) for 0 <= c <= r < T_d is bit r(r+1)/2 + c of
+ * the (doc d, q head h) vector; CA(d,h; c) for 0 <= c < T_d is bit c.  Bit k
+ * is in uint32 word k >> 5 at position k & 31 (LSB first).  Every vector starts
+ * on a word boundary; vectors are stored [global doc][q head][words] with no
+ * gaps.  Bits beyond a vector's length are ignored.  The CA vector of the
+ * last document of a request is read by nobody.
+ *
+ * CSR: rows are ordered h * G + g.  Row (h, g) for tile r of document d lists,
+ * ascending, the global tiles of the CA-marked pages of documents 0..d-1 of
+ * the same request, then the tiles t0_d + c (c <= r) with LA(d,h; r,c) set.
+ * A question tile g lists every tile of its request from the first up to g.
+ * row_ptr is int32 [Hq*G + 1] with row_ptr[0] = 0 and row_ptr[Hq*G] = nnz;
+ * col_idx is int32 [nnz].
+ *
+ * Output: O is fp32 [N][Hq][D]; LSE (optional) is fp32 [Hq][N], natural log.
+ * Padded query tokens and queries with an empty key set get O = 0 and
+ * LSE = -inf.
+ *
+ * Conventions of every call
+ * -------------------------
+ * Ownership: the caller allocates and frees every device buffer (plan,
+ * workspace, inputs, outputs); the library allocates no device memory and keeps
+ * no device state.  Layout arrays are host memory read during the call only.
+ * Asynchrony: work is enqueued on `stream` and the call returns without waiting
+ * for it; results are ready when the stream reaches that point.  The library
+ * never synchronises the device.
+ * Errors: every call validates its host-side arguments first and launches
+ * nothing on error.  Nothing throws across the ABI.
+ */
+#ifndef SIFT_H
+#define SIFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SIFT_OK = 0,
+    SIFT_ERR_INVALID = 1,     /* bad argument: null pointer, inconsistent layout, bad sizes */
+    SIFT_ERR_CAPACITY = 2,    /* a caller buffer is smaller than the size helper requires */
+    SIFT_ERR_UNSUPPORTED = 3, /* valid but unsupported: head_dim not 64/128, tile not 64, int32 overflow */
+    SIFT_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} sift_status;
+
+typedef enum {
+    SIFT_BF16 = 0, /* Q/K/V are bf16 */
+    SIFT_FP32 = 1  /* Q/K/V are fp32; rounded to bf16 (nearest even) on the device first */
+} sift_dtype;
+
+/* One batch of RAG prompts.  All pointers are host memory. */
+typedef struct {
+    int32_t num_requests;          /* >= 1 */
+    const int32_t *req_num_docs;   /* [num_requests], >= 0 */
+    const int32_t *doc_len;        /* [sum req_num_docs], unpadded tokens, >= 1 */
+    const int32_t *question_len;   /* [num_requests], unpadded tokens, >= 0 */
+    int32_t num_q_heads;           /* Hq >= 1 */
+    int32_t num_kv_heads;          /* Hkv >= 1, Hq % Hkv == 0 */
+    int32_t head_dim;              /* D: 64 or 128 */
+    int32_t tile;                  /* must be 64 */
+} sift_layout;
+
+/* ---- sizing helpers: return -1 (or 0 for size_t) if the layout is invalid ---- */
+
+int64_t sift_num_tiles(const sift_layout *layout);     /* G */
+int64_t sift_padded_tokens(const sift_layout *layout); /* N = 64 G */
+int64_t sift_num_rows(const sift_layout *layout);      /* Hq * G */
+int64_t sift_la_words(const sift_layout *layout);      /* uint32 words of all LA vectors */
+int64_t sift_ca_words(const sift_layout *layout);      /* uint32 words of all CA vectors */
+/* Upper bound of nnz: the count with every bit set (dense causal tiles). */
+int64_t sift_csr_max_nnz(const sift_layout *layout);
+/* Bytes of the device plan written by sift_plan_upload. */
+size_t sift_plan_bytes(const sift_layout *layout);
+/* Bytes of device scratch that sift_decode_bits / sift_sparse_prefill need. */
+size_t sift_workspace_bytes(const sift_layout *layout, sift_dtype dtype);
+
+/*
+ * sift_plan_upload: write the layout's device tables (per-tile segment data,
+ * per-document bit offsets, per-request first tiles) into d_plan, a caller
+ * buffer of at least sift_plan_bytes() bytes, with one hipMemcpyAsync on
+ * `stream` from a host staging copy.  A plan depends on the layout only, so one
+ * upload serves every layer of a batch.  The plan carries a fingerprint of the
+ * layout; decode and prefill launched with a plan of another layout do nothing
+ * on the device (and the host check cannot see this), so keep them paired.
+ * Errors: SIFT_ERR_INVALID (layout, null), SIFT_ERR_CAPACITY (plan_bytes),
+ * SIFT_ERR_HIP.
+ */
+sift_status sift_plan_upload(const sift_layout *layout, void *d_plan, size_t plan_bytes,
+                             hipStream_t stream);
+
+/*
+ * sift_decode_bits: the decode kernel of the technical summary's
+ * "Dettagli di Implementazione" -- expand one layer's LA and CA bit vectors
+ * (device, sift_la_words / sift_ca_words uint32 words) into the CSR described
+ * above: d_row_ptr int32 [Hq*G + 1] and d_col_idx int32 [col_capacity].
+ * col_capacity must be >= sift_csr_max_nnz(), which makes the fill safe
+ * without a host read-back of nnz (nnz is row_ptr[Hq*G] on the device).
+ * d_workspace: >= sift_workspace_bytes(layout, SIFT_BF16) bytes of scratch.
+ * Errors: SIFT_ERR_INVALID, SIFT_ERR_CAPACITY (col_capacity, workspace),
+ * SIFT_ERR_UNSUPPORTED (nnz bound >= 2^31), SIFT_ERR_HIP.
+ */
+sift_status sift_decode_bits(const sift_layout *layout, const void *d_plan,
+                             const uint32_t *d_la, const uint32_t *d_ca,
+                             int32_t *d_row_ptr, int32_t *d_col_idx, int64_t col_capacity,
+                             void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sift_sparse_prefill: the sparse attention kernel of "Dettagli di
+ * Implementazione" -- block-sparse causal GQA attention with online softmax
+ * that, for each row (h, g), visits only the KV tiles listed in the CSR.
+ * scores = scale * q.k (scale <= 0 selects 1/sqrt(head_dim)), bf16 MFMA with
+ * fp32 accumulation, fp32 softmax, fp32 output d_out [N][Hq][D]; d_lse
+ * [Hq][N] may be NULL.  Listed tiles outside [0, G) are skipped.  For
+ * SIFT_FP32 inputs the workspace holds their bf16 copies.
+ * Errors: SIFT_ERR_INVALID, SIFT_ERR_CAPACITY (workspace),
+ * SIFT_ERR_UNSUPPORTED (head_dim, tile), SIFT_ERR_HIP.
+ */
+sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan,
+                                const void *d_q, const void *d_k, const void *d_v, sift_dtype dtype,
+                                const int32_t *d_row_ptr, const int32_t *d_col_idx, float scale,
+                                float *d_out, float *d_lse,
+                                void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *sift_status_string(sift_status status);
+
+/* Version of this ABI: (major << 16) | minor. */
+int32_t sift_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SIFT_H */

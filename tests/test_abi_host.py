@@ -1,0 +1,137 @@
+"""The C ABI on the host (no GPU calls): exports, sizing helpers and validation."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import bit_vector_block_amd as sift
+from bit_vector_block_amd import _binding as B
+from bit_vector_block_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "sift.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sift_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sift.library()
+    declared = _declared_functions()
+    assert len(declared) >= 13
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(B.EXPORTED) == declared
+    assert lib.sift_abi_version() >> 16 == 1
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_sizing_helpers_match_the_generator(cid):
+    case = W.config_case(cid)
+    lay = sift.Layout.from_case(case)
+    assert lay.padded_tokens == case.q.shape[0]
+    assert lay.num_tiles * 64 == case.q.shape[0]
+    assert lay.num_rows == lay.num_tiles * case.num_q_heads
+    assert lay.la_words == case.la_words.size
+    assert lay.ca_words == case.ca_words.size
+
+
+@pytest.mark.parametrize("cid,G,la_words,ca_words", [
+    (3, 516, 32 * 32 * 5, 32 * 32), (4, 644, 20 * 64 * 17, 20 * 64)])
+def test_sizing_of_large_workloads(cid, G, la_words, ca_words):
+    r, dl, ql, hq, hkv, d = W.config_layout(cid)
+    lay = sift.Layout(r, dl, ql, hq, hkv, d)
+    assert lay.num_tiles == G and lay.la_words == la_words and lay.ca_words == ca_words
+
+
+def test_ragged_layout_matches_the_case_draw():
+    r, dl, ql, hq, hkv, d = W.config_layout(5)
+    lay = sift.Layout(r, dl, ql, hq, hkv, d)
+    assert lay.padded_tokens == W.padded_total(r, dl, ql)
+    assert lay.padded_tokens > 100_000
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_max_nnz_is_the_all_ones_count(seed):
+    case = W.random_small_case(seed, max_requests=3, max_docs=4, hq=3, hkv=1, d=64)
+    ones = W.with_bits(case, *W.all_ones_bits(case))
+    lay = sift.Layout.from_case(case)
+    assert lay.csr_max_nnz == int(oracle.row_counts(ones).sum())
+    assert lay.csr_max_nnz >= int(oracle.row_counts(case).sum())
+    assert lay.la_words == case.la_words.size and lay.ca_words == case.ca_words.size
+
+
+def _status(lay, **kw):
+    lib = sift.library()
+    args = dict(plan=1, la=1, ca=1, row_ptr=1, col_idx=1, ws=1, ws_bytes=lay.workspace_bytes())
+    args.update(kw)
+    if "cap" not in args:
+        args["cap"] = lay.csr_max_nnz
+    vp = ctypes.c_void_p
+    return lib.sift_decode_bits(lay.ref, vp(args["plan"]), vp(args["la"]), vp(args["ca"]),
+                                vp(args["row_ptr"]), vp(args["col_idx"]), args["cap"], vp(args["ws"]),
+                                args["ws_bytes"], vp(0))
+
+
+def test_decode_validation_rejects_before_any_launch():
+    case = W.random_small_case(3, d=64)
+    lay = sift.Layout.from_case(case)
+    assert _status(lay, plan=0) == B.SIFT_ERR_INVALID
+    assert _status(lay, row_ptr=0) == B.SIFT_ERR_INVALID
+    assert _status(lay, la=0) == B.SIFT_ERR_INVALID
+    assert _status(lay, cap=lay.csr_max_nnz - 1) == B.SIFT_ERR_CAPACITY
+    assert _status(lay, ws_bytes=0) == B.SIFT_ERR_CAPACITY
+    assert _status(lay, ws=0) == B.SIFT_ERR_CAPACITY
+
+
+def test_prefill_validation_rejects_before_any_launch():
+    case = W.random_small_case(4, d=64)
+    lay = sift.Layout.from_case(case)
+    lib = sift.library()
+    vp = ctypes.c_void_p
+    st = lib.sift_sparse_prefill(lay.ref, vp(1), vp(0), vp(1), vp(1), B.SIFT_BF16, vp(1), vp(1),
+                                 ctypes.c_float(0.0), vp(1), vp(0), vp(0), 0, vp(0))
+    assert st == B.SIFT_ERR_INVALID
+    st = lib.sift_sparse_prefill(lay.ref, vp(1), vp(1), vp(1), vp(1), 7, vp(1), vp(1),
+                                 ctypes.c_float(0.0), vp(1), vp(0), vp(0), 0, vp(0))
+    assert st == B.SIFT_ERR_INVALID
+    # fp32 inputs need workspace for their bf16 copies
+    st = lib.sift_sparse_prefill(lay.ref, vp(1), vp(1), vp(1), vp(1), B.SIFT_FP32, vp(1), vp(1),
+                                 ctypes.c_float(0.0), vp(1), vp(0), vp(0), 0, vp(0))
+    assert st == B.SIFT_ERR_CAPACITY
+    assert lay.workspace_bytes(B.SIFT_FP32) >= 2 * lay.padded_tokens * (lay.num_q_heads + 2 * lay.num_kv_heads) * lay.head_dim
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(num_q_heads=3, num_kv_heads=2), B.SIFT_ERR_INVALID),
+    (dict(head_dim=96), B.SIFT_ERR_UNSUPPORTED),
+    (dict(tile=32), B.SIFT_ERR_UNSUPPORTED),
+    (dict(doc_len=[100, 0]), B.SIFT_ERR_INVALID),
+    (dict(question_len=[-1]), B.SIFT_ERR_INVALID),
+])
+def test_invalid_layouts(kw, expect):
+    base = dict(req_num_docs=[2], doc_len=[100, 70], question_len=[10], num_q_heads=4,
+                num_kv_heads=2, head_dim=64, tile=64)
+    base.update(kw)
+    lay = sift.Layout(**base)
+    assert sift.library().sift_num_tiles(lay.ref) == -1
+    assert lay.plan_bytes == 0
+    assert _status(lay, cap=0) == expect
+
+
+def test_int32_overflow_is_unsupported():
+    # one request of 4M tokens: the dense-causal CSR bound passes 2^31 entries
+    lay = sift.Layout([1], [4_000_000], [0], 32, 8, 128)
+    assert sift.library().sift_num_tiles(lay.ref) == -1
+    assert _status(lay, cap=0) == B.SIFT_ERR_UNSUPPORTED
+
+
+def test_empty_layout_sizes():
+    lay = sift.Layout([0], [], [0], 2, 1, 64)
+    assert lay.num_tiles == 0 and lay.num_rows == 0 and lay.csr_max_nnz == 0
+    assert lay.plan_bytes > 0 and lay.workspace_bytes() > 0

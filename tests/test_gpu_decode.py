@@ -1,0 +1,101 @@
+"""GPU decode kernel vs the oracle: the CSR must be bit-exact (row_ptr and col_idx)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_vector_block_amd import workloads as W
+from gpu_common import config, gpu_decode
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _check(case, **kw):
+    rp, ci = gpu_decode(case, **kw)
+    orp, oci = oracle.decode(case, **kw)
+    assert rp.shape == orp.shape and np.array_equal(rp, orp), "row_ptr differs"
+    assert ci.shape == oci.shape and np.array_equal(ci, oci), "col_idx differs"
+    return rp, ci
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_decode_configs_bit_exact(cid):
+    case = config(cid)
+    print(f"decode config {cid}: G={case.q.shape[0] // 64} Hq={case.num_q_heads}", flush=True)
+    _check(case)
+
+
+def test_decode_hand_worked_example():
+    with open(os.path.join(GOLDEN, "hand_decode_example.json")) as f:
+        g = json.load(f)
+    case = W.make_case("golden", 0, g["req_num_docs"], g["doc_len"], g["question_len"],
+                       g["num_q_heads"], 1, 64, np.zeros((2, 2)), np.zeros((2, 2)))
+    case.la_words = np.array(g["la_words"], np.uint32)
+    case.ca_words = np.array(g["ca_words"], np.uint32)
+    rp, ci = gpu_decode(case)
+    assert rp.tolist() == g["row_ptr"] and ci.tolist() == g["col_idx"]
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_decode_random_small(seed):
+    case = W.random_small_case(seed, max_requests=3, max_docs=5, max_tiles=6, hq=1 + seed % 4,
+                               hkv=1, d=64)
+    _check(case)
+
+
+@pytest.mark.parametrize("tiles", [31, 32, 33, 47, 64, 65, 100])
+def test_decode_multiword_vectors(tiles):
+    """Documents whose LA/CA vectors span several words (T not a multiple of 32)."""
+    case = W.make_case("mw", tiles, [3], [64 * tiles - 5, 64 * tiles, 70], [100], 2, 1, 64,
+                       np.full((1, 2), 0.3), np.full((1, 2), 0.4))
+    _check(case)
+
+
+@pytest.mark.parametrize("pattern", ["zeros", "ones", "single", "last_bits"])
+def test_decode_adversarial_bits(pattern):
+    case = W.make_case("adv", 5, [2, 3], [2000, 64, 900, 1, 3000], [65, 0], 3, 1, 64,
+                       np.full((2, 3), 0.5), np.full((2, 3), 0.5))
+    la, ca = case.la_words.copy(), case.ca_words.copy()
+    if pattern == "zeros":
+        la[:] = 0
+        ca[:] = 0
+    elif pattern == "ones":
+        la[:] = 0xFFFFFFFF  # includes every unused high bit
+        ca[:] = 0xFFFFFFFF
+    elif pattern == "single":
+        la[:] = 0
+        ca[:] = 0
+        la[len(la) // 2] = 1 << 7
+        ca[len(ca) // 3] = 1 << 2
+    else:  # only bit 31 of every word
+        la[:] = 1 << 31
+        ca[:] = 1 << 31
+    _check(case, la_words=la, ca_words=ca)
+
+
+def test_decode_ignores_unused_high_bits():
+    case = W.make_case("hb", 7, [3], [130, 64 * 33 + 1, 64], [10], 2, 1, 64,
+                       np.full((1, 2), 0.3), np.full((1, 2), 0.3))
+    la, ca = case.la_words.copy(), case.ca_words.copy()
+    la |= np.uint32(0x80000000)
+    ca |= np.uint32(0x80000000)
+    # these may or may not be unused bits; the oracle reads the same words
+    _check(case, la_words=la, ca_words=ca)
+
+
+def test_decode_question_only_and_docs_only():
+    a = W.make_case("q", 8, [0], [], [300], 2, 1, 64, np.full((1, 2), 0.5), np.full((1, 2), 0.5))
+    _check(a)
+    b = W.make_case("q2", 9, [0, 2], [500, 90], [300, 0], 2, 1, 64, np.full((2, 2), 0.5),
+                    np.full((2, 2), 0.5))
+    _check(b)
+
+
+def test_decode_empty_layout():
+    case = W.make_case("empty", 10, [0], [], [0], 2, 1, 64, np.zeros((1, 2)), np.zeros((1, 2)))
+    rp, ci = gpu_decode(case)
+    assert rp.tolist() == [0] and ci.size == 0

@@ -1,0 +1,128 @@
+"""GPU sparse prefill vs the fp64 oracle (max-abs 1e-2, mean-abs 1e-3) and exact properties."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_vector_block_amd import workloads as W
+from gpu_common import LSE_ABS, assert_close, config, gpu_prefill, valid_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_check(case):
+    out, lse = gpu_prefill(case)
+    ref, ref_lse = oracle.attention(case)
+    valid = valid_tokens(case)
+    mx, mean = assert_close(out[valid], ref[valid], case.name)
+    assert np.all(out[~valid] == 0.0), "padded query rows must be exactly 0"
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.max(np.abs(lse[fin] - ref_lse[fin]), initial=0.0) <= LSE_ABS
+    return mx, mean
+
+
+def test_prefill_tiny_config_fp32_inputs():
+    """Config 1: fp32 Q/K/V, rounded to bf16 on the device, vs the oracle on the same rounding."""
+    case = config(1)
+    mx, mean = _full_check(case)
+    print(f"tiny: max_abs {mx:.3e} mean_abs {mean:.3e}")
+    # informational: distance to the oracle on the unrounded fp32 inputs
+    out, _ = gpu_prefill(case, want_lse=False)
+    exact, _ = oracle.attention(case, exact_fp32=True)
+    valid = valid_tokens(case)
+    print(f"tiny vs unrounded fp32 oracle: max_abs {np.abs(out[valid] - exact[valid]).max():.3e}")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_prefill_random_small(seed):
+    d = 64 if seed % 2 else 128
+    hq, hkv = [(1, 1), (4, 2), (4, 1), (8, 2), (2, 2)][seed % 5]
+    case = W.random_small_case(seed, max_requests=3, max_docs=4, max_tiles=5, hq=hq, hkv=hkv, d=d)
+    _full_check(case)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_prefill_all_ones_is_dense_causal(seed):
+    case = W.random_small_case(50 + seed, hq=4, hkv=2, d=128, max_tiles=6)
+    case = W.with_bits(case, *W.all_ones_bits(case))
+    _full_check(case)
+
+
+def _sample_pairs(case, rng, n_random):
+    """(head, token) pairs: random valid tokens, the first and last tiles, a strided sweep."""
+    valid = np.where(valid_tokens(case))[0]
+    toks = [rng.choice(valid, size=n_random)]
+    n = case.q.shape[0]
+    # first and last 64 tokens of the sequence, plus a strided sweep
+    toks.append(np.arange(0, min(64, n)))
+    toks.append(np.arange(max(0, n - 64), n))
+    toks.append(np.arange(0, n, 997))
+    toks = np.concatenate(toks)
+    heads = rng.integers(0, case.num_q_heads, size=toks.size)
+    return heads.astype(np.int32), toks.astype(np.int64)
+
+
+@pytest.mark.parametrize("cid,n_random", [(2, 3000), (3, 1500), (4, 1000), (5, 600)])
+def test_prefill_configs_sampled(cid, n_random):
+    case = config(cid)
+    print(f"prefill config {cid}: N={case.q.shape[0]} Hq={case.num_q_heads}", flush=True)
+    out, lse = gpu_prefill(case)
+    valid = valid_tokens(case)
+    assert np.all(np.isfinite(out)), "non-finite output"
+    assert np.all(out[~valid] == 0.0), "padded query rows must be exactly 0"
+    rng = np.random.default_rng(cid)
+    heads, toks = _sample_pairs(case, rng, n_random)
+    ref, ref_lse = oracle.attention(case, heads=heads, tokens=toks)
+    got = out[toks, heads]
+    keep = valid[toks]
+    mx, mean = assert_close(got[keep], ref[keep], f"config {cid}")
+    fin = np.isfinite(ref_lse)
+    assert np.max(np.abs(lse[heads, toks][fin] - ref_lse[fin]), initial=0.0) <= LSE_ABS
+    print(f"config {cid}: {keep.sum()} sampled rows, max_abs {mx:.3e} mean_abs {mean:.3e}")
+
+
+def test_prefill_single_key_is_exact():
+    """P7 on the GPU: the first token of doc 0 sees only itself, so O = v_0 exactly."""
+    case = W.make_case("p7", 700, [2], [100, 70], [30], 2, 1, 128, [[0.3, 0.3]], [[0.5, 0.5]])
+    out, lse = gpu_prefill(case)
+    v0 = W.bf16_bits_to_f32(case.v[0, 0])
+    assert np.array_equal(out[0, 0], v0) and np.array_equal(out[0, 1], v0)
+
+
+def test_prefill_locality_poisoned_tiles():
+    """P8: NaN in K/V of every tile a row does not list, NaN in padded K slots and +-1e4 in
+    padded V slots leave that row's output finite and bit-identical."""
+    case = W.make_case("p8", 800, [3], [150, 64, 100], [40], 2, 1, 128,
+                       np.full((1, 2), 0.4), np.full((1, 2), 0.4))
+    out0, _ = gpu_prefill(case, want_lse=False)
+    rp, ci = oracle.decode(case)
+    G = case.q.shape[0] // 64
+    valid = valid_tokens(case)
+    nan16 = np.uint16(0x7FC0)
+    big = W.f32_to_bf16_bits(np.array([1e4], np.float32))[0]
+    for h in range(case.num_q_heads):
+        for g in range(G):
+            listed = set(ci[rp[h * G + g]: rp[h * G + g + 1]].tolist())
+            k, v = case.k.copy(), case.v.copy()
+            for t in range(G):
+                if t not in listed:
+                    k[64 * t: 64 * t + 64] = nan16
+                    v[64 * t: 64 * t + 64] = nan16
+            pad = ~valid
+            k[pad] = nan16
+            v[pad] = big
+            out, _ = gpu_prefill(case, k=k, v=v, want_lse=False)
+            sl = slice(64 * g, 64 * g + 64)
+            assert np.array_equal(out[sl, h], out0[sl, h]), f"row (h={h}, g={g}) changed"
+
+
+def test_prefill_empty_rows():
+    """Rows with no listed tiles give O = 0 and LSE = -inf."""
+    case = W.make_case("empty-rows", 900, [2], [200, 64], [0], 2, 1, 64, np.zeros((1, 2)), np.zeros((1, 2)))
+    la = [np.zeros_like(x) for x in case.la_bool]
+    ca = [np.zeros_like(x) for x in case.ca_bool]
+    case = W.with_bits(case, la, ca)
+    out, lse = gpu_prefill(case)
+    assert np.all(out == 0.0) and np.all(np.isneginf(lse))
