@@ -122,6 +122,8 @@ def main(argv=None):
                     help="synthetic workload id (2 = the Llama-3.1-8B 10 x 1K layer)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU work budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--no-full-recompute", action="store_true",
+                    help="skip the full-recompute comparison (same kernels on all-ones bits)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run plain device copies of this many MiB "
                          "(reference reading for the HBM byte counters)")
@@ -174,36 +176,38 @@ def main(argv=None):
     out = torch.empty((N, Hq, D), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        sift.decode_bits(lay, la, ca, plan=plan, workspace=ws, row_ptr=row_ptr, col_idx=col_idx)
-        if ev is not None:
-            ev[1].record(stream)
-        sift.sparse_prefill(lay, q, k, v, row_ptr, col_idx, plan=plan, workspace=ws, out=out)
-        if ev is not None:
-            ev[2].record(stream)
+    def timed(la_d, ca_d, steps, warmup):
+        """Warm up, then time `steps` layer steps (decode + prefill) on the launch stream."""
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            sift.decode_bits(lay, la_d, ca_d, plan=plan, workspace=ws, row_ptr=row_ptr, col_idx=col_idx)
+            if ev is not None:
+                ev[1].record(stream)
+            sift.sparse_prefill(lay, q, k, v, row_ptr, col_idx, plan=plan, workspace=ws, out=out)
+            if ev is not None:
+                ev[2].record(stream)
 
-    log(f"warmup {args.warmup}")
-    for _ in range(max(args.warmup, 1)):
-        step()
-    torch.cuda.synchronize()
+        for _ in range(max(warmup, 1)):
+            step()
+        torch.cuda.synchronize()
+        nnz_ = int(row_ptr[-1].item())
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(steps):
+            step(evs[i])
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        return (nnz_, t_start.elapsed_time(t_end) / steps,
+                float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+                float(np.mean([e[1].elapsed_time(e[2]) for e in evs])))
+
+    log(f"warmup {args.warmup}, timing {args.steps} steps")
+    nnz, ms_per_step, decode_ms, prefill_ms = timed(la, ca, args.steps, args.warmup)
     rp_host = row_ptr.cpu().numpy().astype(np.int64)
-    nnz = int(rp_host[-1])
-
-    log(f"timing {args.steps} steps")
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    decode_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    prefill_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
 
     flops = float(nnz) * 4.0 * 64 * 64 * D
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -248,6 +252,19 @@ def main(argv=None):
             "traffic": profiled_traffic(args.workload),
         },
     }
+    if not args.no_full_recompute:
+        # the pages' speed reference: full recompute = dense causal prefill, here the same
+        # kernels on all-ones bits
+        log("full-recompute comparison (all-ones bits)")
+        dense = W.with_bits(case, *W.all_ones_bits(case))
+        la1, ca1 = to_dev_words(dense.la_words), to_dev_words(dense.ca_words)
+        nnz1, ms1, dec1, pre1 = timed(la1, ca1, max(3, args.steps // 5), 2)
+        result["full_recompute"] = {
+            "ms_per_layer": round(ms1, 5),
+            "computed_tiles": nnz1,
+            "tflops": round(float(nnz1) * 4.0 * 64 * 64 * D / (pre1 * 1e-3) / 1e12, 3),
+            "speedup_of_sparse_layer": round(ms1 / ms_per_step, 3),
+        }
     if args.cpu_seconds > 0:
         log(f"cpu baseline (~{args.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(case, rp_host, args.cpu_seconds)

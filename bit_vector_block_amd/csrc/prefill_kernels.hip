@@ -358,7 +358,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     {
         const uint16_t *qrow = q + ((tok0 + qi) * Hq + h) * D + 8 * hi;
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) st.qf[dc] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * dc);
+        for (int dc = 0; dc < DC; ++dc)  // read once: stream it past L2 (keep L2 for K/V tiles)
+            st.qf[dc] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(qrow + 16 * dc));
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db) st.acc_o[db] = f32x16{};
@@ -488,7 +489,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int r = x / C4, c4 = x % C4;
         f32x4 val = *reinterpret_cast<const f32x4 *>(orow(r) + 4 * (c4 ^ (r & (C4 - 1))));
         if (r >= q_valid) val = f32x4{};
-        *reinterpret_cast<f32x4 *>(out + ((tok0 + r) * Hq + h) * D + 4 * c4) = val;
+        // written once: non-temporal, so 32 KB of output per row does not evict K/V tiles
+        __builtin_nontemporal_store(val, reinterpret_cast<f32x4 *>(out + ((tok0 + r) * Hq + h) * D + 4 * c4));
     }
 }
 

@@ -6,7 +6,8 @@ import pytest
 
 import oracle
 from bit_vector_block_amd import workloads as W
-from gpu_common import LSE_ABS, assert_close, config, gpu_prefill, valid_tokens
+import bit_vector_block_amd as sift
+from gpu_common import LSE_ABS, assert_close, config, gpu_decode, gpu_prefill, valid_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +82,26 @@ def test_prefill_configs_sampled(cid, n_random):
     fin = np.isfinite(ref_lse)
     assert np.max(np.abs(lse[heads, toks][fin] - ref_lse[fin]), initial=0.0) <= LSE_ABS
     print(f"config {cid}: {keep.sum()} sampled rows, max_abs {mx:.3e} mean_abs {mean:.3e}")
+
+
+def test_prefill_full_recompute_config2_sampled():
+    """Full recompute (every LA and CA bit set, i.e. dense causal attention per request) at the
+    10 x 1k-token, 32/8-head, d=128 size, through the same decode and prefill launches."""
+    case = config(2)
+    case = W.with_bits(case, *W.all_ones_bits(case))
+    rp, ci = gpu_decode(case)
+    lay = sift.Layout.from_case(case)
+    assert rp[-1] == lay.csr_max_nnz, "all-ones bits must give the dense causal tile count"
+    out, lse = gpu_prefill(case)
+    valid = valid_tokens(case)
+    rng = np.random.default_rng(22)
+    heads, toks = _sample_pairs(case, rng, 1500)
+    ref, ref_lse = oracle.attention(case, heads=heads, tokens=toks)
+    keep = valid[toks]
+    mx, mean = assert_close(out[toks, heads][keep], ref[keep], "full recompute, config 2")
+    fin = np.isfinite(ref_lse)
+    assert np.max(np.abs(lse[heads, toks][fin] - ref_lse[fin]), initial=0.0) <= LSE_ABS
+    print(f"full recompute: {keep.sum()} sampled rows, max_abs {mx:.3e} mean_abs {mean:.3e}")
 
 
 def test_prefill_single_key_is_exact():
