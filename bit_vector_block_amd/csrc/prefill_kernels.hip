@@ -10,16 +10,23 @@
 //    wavefronts: wave w takes queries 32 (w & 1) .. +31 and, of every listed
 //    KV tile, keys 32 (w >> 1) .. +31.  Each wave keeps its own online-softmax
 //    state; the two key halves are merged once at the end;
-//  * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
+//  * V is first rewritten as V^T ([kv head][D][N], one pass over V per call)
+//    with the tokens of every 16-token group stored in the order the PV
+//    operands consume them, so that every MFMA operand -- K for the scores,
+//    V^T for the output -- is one 16-byte LDS read per lane;
+//  * K and V^T tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
 //    register staging), double buffered so the next listed tile streams in
-//    while the current one is multiplied.  16-byte chunks are XOR-swizzled per
-//    row so that the MFMA operand reads below are free of bank conflicts;
+//    while the current one is multiplied.  K rows are padded by 16 bytes and
+//    V^T 16-byte chunks are XOR-swizzled per row, so the operand reads are free
+//    of bank conflicts and K's need a single address register;
 //  * scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    lane l then holds 16 keys of query (l % 32); the online-softmax state of
-//    a query lives in lanes l and l ^ 32;
-//  * the output is accumulated transposed, O^T += V^T P^T: the B operand is the
-//    lane's own P values, and the V^T operand comes from ds_read_b64_tr_b16
-//    (a 16-lane transposing LDS read) on the row-major V tile;
+//    a query lives in lanes l and l ^ 32; the output is accumulated
+//    transposed, O^T += V^T P^T, whose B operand is the lane's own P values;
+//  * one pipeline step issues all operand reads of the step first, then the
+//    score MFMAs of the next tile interleaved (pinned with scheduling
+//    barriers) with the exponentials of the current tile, then the output
+//    MFMAs of the current tile interleaved with the max tree of the next;
 //  * exp2 with log2(e) folded into the scale; the running maximum is raised
 //    (and O, l rescaled) only when a tile's maximum exceeds it by more than
 //    kLazyLog2 in log2 units, which bounds P by 2^kLazyLog2 and leaves
@@ -40,13 +47,10 @@ namespace sift {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 typedef const __attribute__((address_space(4))) int32_t const_i32;
 
@@ -61,6 +65,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLazyLog2 = 8.0f;
 constexpr int kXcds = 8;
+constexpr int kPersistentPerXcd = 64;  // 2 workgroups on each of the 32 CUs of an XCD
 
 __device__ inline bool plan_ok(const PlanView &pv) {
     return pv.header[0] == static_cast<int32_t>(kPlanMagic) &&
@@ -70,22 +75,26 @@ __device__ inline bool plan_ok(const PlanView &pv) {
 
 template <int D>
 struct Cfg {
-    static constexpr int CPR = D / 8;                        // 16-byte chunks per K/V row
-    static constexpr int TILE = 64 * D;                      // bf16 elements per K or V tile
-    static constexpr int RPL = 64 / CPR;                     // rows per 64-lane load
-    static constexpr int LOADS = 64 * CPR / (64 * kWaves);   // loads per wave per matrix per tile
-    static constexpr int BUF = 2 * TILE;                     // K then V
-    static_assert(32 * D * 4 == TILE * 2, "32 fp32 output rows fill one tile buffer");
+    static constexpr int CPR = D / 8;                   // 16-byte chunks per K row
+    static constexpr int KROW = 2 * D + 16;             // LDS bytes per K row (16 bytes of padding)
+    static constexpr int KBYTES = 64 * KROW;            // LDS bytes per K tile
+    static constexpr int KLOADS = KBYTES / 1024;        // 1 KB loads per K tile (17 or 9)
+    static constexpr int KLOADS_W = (KLOADS + kWaves - 1) / kWaves;  // per wave, at most
+    static constexpr int VBYTES = 128 * D;              // LDS bytes per V^T tile (D rows x 64 tokens)
+    static constexpr int VLOADS_W = VBYTES / 1024 / kWaves;  // 1 KB loads per wave per V^T tile
+    static constexpr int DC = D / 16;                   // MFMA K-steps of the scores
+    static constexpr int DB = D / 32;                   // 32-row blocks of O^T
+    static_assert(KBYTES % 1024 == 0 && VBYTES % (1024 * kWaves) == 0, "whole 1 KB loads");
+    static_assert(32 * D * 4 <= KBYTES, "32 fp32 output rows fit one K buffer");
 };
+// slot of 16-byte chunk c in V^T row d (64 tokens = 8 chunks per row): the 16 lanes of one
+// LDS cycle read rows d0 .. d0 + 15 at one chunk; (d & 1, (d >> 1) & 7) is distinct over them
+__device__ inline int vt_slot(int d, int c) { return c ^ ((d >> 1) & 7); }
 
-// slot of 16-byte chunk c in K row r / V row r
-template <int D>
-__device__ inline int k_slot(int r, int c) { return c ^ (r & (Cfg<D>::CPR - 1)); }
-// V rows: the transposing reads of one K-step touch 4 consecutive rows x 2 (16 lanes) or
-// 4 (32 lanes) consecutive chunks; XOR masks {0, 6, 12, 10} keep those 8 (or 16) chunks
-// on distinct banks for 128-byte and 256-byte LDS cycles alike.
-template <int D>
-__device__ inline int v_slot(int r, int c) { return c ^ ((0xAC60 >> (4 * (r & 3))) & 15 & (Cfg<D>::CPR - 1)); }
+// position of token n inside V^T: bits 2 and 3 of n swapped, so that within every 16-token
+// group the 8 tokens {0..3, 8..11} come first and {4..7, 12..15} second -- the 8 keys that
+// lane half 0 and lane half 1 feed into one PV K-step
+__host__ __device__ inline int64_t vt_pos(int64_t n) { return (n & ~int64_t(12)) | ((n & 4) << 1) | ((n & 8) >> 1); }
 
 __device__ inline void wait_vmcnt_le(int n) {
     // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt at their maxima)
@@ -94,40 +103,61 @@ __device__ inline void wait_vmcnt_le(int n) {
     else __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
 }
 
-// Per-lane byte offsets of this lane's direct-to-LDS loads inside a K or V tile
-// (the same for every tile; the tile itself only moves a uniform base pointer).
+// Per-lane byte offsets of this lane's direct-to-LDS loads inside a K tile and a V^T tile
+// (the same for every tile; the tile itself only moves a uniform base pointer).  A load
+// writes lane i's 16 bytes at LDS offset 16 i of its 1 KB destination, so the layout is
+// applied on the global side: lane i fetches the chunk that belongs at that LDS position.
+// Wave w issues K loads w, w + 4, ...; a lane whose position is a K row's padding fetches
+// chunk 0 of that row again (never read).
 template <int D>
 struct LoadOffsets {
-    uint32_t k[Cfg<D>::LOADS];
-    uint32_t v[Cfg<D>::LOADS];
+    uint32_t k[Cfg<D>::KLOADS_W];
+    uint32_t v[Cfg<D>::VLOADS_W];
 };
 
 template <int D>
-__device__ inline LoadOffsets<D> make_load_offsets(int Hkv, int wave, int lane) {
+__device__ inline LoadOffsets<D> make_load_offsets(int Hkv, int64_t N, int wave, int lane) {
     using C = Cfg<D>;
     LoadOffsets<D> o;
-    const uint32_t row_bytes = static_cast<uint32_t>(Hkv) * D * 2;
+    const uint32_t krow_bytes = static_cast<uint32_t>(Hkv) * D * 2;
+    const uint32_t vrow_bytes = static_cast<uint32_t>(N) * 2;
 #pragma unroll
-    for (int j = 0; j < C::LOADS; ++j) {
-        const int I = wave * C::LOADS + j;  // this load fills LDS elements [512 I, 512 I + 512)
-        const int r = I * C::RPL + lane / C::CPR;
-        const int sl = lane % C::CPR;       // LDS slot written by this lane
-        o.k[j] = r * row_bytes + 16u * static_cast<uint32_t>(k_slot<D>(r, sl));
-        o.v[j] = r * row_bytes + 16u * static_cast<uint32_t>(v_slot<D>(r, sl));
+    for (int j = 0; j < C::KLOADS_W; ++j) {
+        const int b = 1024 * (wave + kWaves * j) + 16 * lane;  // LDS byte this lane fills
+        const int r = b / C::KROW, c = (b % C::KROW) / 16;
+        o.k[j] = r * krow_bytes + 16u * static_cast<uint32_t>(c < C::CPR ? c : 0);
+    }
+#pragma unroll
+    for (int j = 0; j < C::VLOADS_W; ++j) {
+        const int I = wave * C::VLOADS_W + j;  // this load fills V^T tile bytes [1024 I, 1024 I + 1024)
+        const int d = I * 8 + lane / 8;
+        o.v[j] = d * vrow_bytes + 16u * static_cast<uint32_t>(vt_slot(d, lane % 8));
     }
     return o;
 }
 
-// Direct-to-LDS load of one K (or V) tile starting at token ktok0 into `dst`.
+// Direct-to-LDS load of one K tile (base = the tile's first token row of this kv head).
 template <int D>
-__device__ __forceinline__ void load_half(const uint16_t *__restrict__ src, int64_t ktok0, int Hkv,
-                                          int kvh, uint16_t *dst, int wave, const uint32_t *off) {
+__device__ __forceinline__ void load_k_tile(const uint16_t *base, char *dst, int wave, const uint32_t *off) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot type-check this builtin
     using C = Cfg<D>;
-    const char *g = reinterpret_cast<const char *>(src + (ktok0 * Hkv + kvh) * D);  // uniform
+    const char *g = reinterpret_cast<const char *>(base);  // uniform
 #pragma unroll
-    for (int j = 0; j < C::LOADS; ++j)
-        __builtin_amdgcn_global_load_lds(g + off[j], (lds_void *)(dst + 512 * (wave * C::LOADS + j)), 16, 0, 0);
+    for (int j = 0; j < C::KLOADS_W; ++j)
+        if (wave + kWaves * j < C::KLOADS)
+            __builtin_amdgcn_global_load_lds(g + off[j], (lds_void *)(dst + 1024 * (wave + kWaves * j)), 16, 0, 0);
+#endif
+}
+
+// Direct-to-LDS load of one V^T tile (base = row d = 0 of this kv head at the tile's first token).
+template <int D>
+__device__ __forceinline__ void load_vt_tile(const uint16_t *base, char *dst, int wave, const uint32_t *off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = Cfg<D>;
+    const char *g = reinterpret_cast<const char *>(base);  // uniform
+#pragma unroll
+    for (int j = 0; j < C::VLOADS_W; ++j)
+        __builtin_amdgcn_global_load_lds(g + off[j], (lds_void *)(dst + 1024 * (wave * C::VLOADS_W + j)), 16, 0, 0);
 #endif
 }
 
@@ -141,6 +171,14 @@ __device__ inline float pair_sum(float x) {  // sum over lanes l and l ^ 32
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// max of three without the NaN-quieting canonicalisations fmaxf brings; inputs are MFMA
+// results or -inf from masking, and a NaN score can only come from masked padded keys
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Online-softmax state of one wavefront (32 queries x one 32-key half of each tile).
 template <int D>
 struct WaveState {
@@ -151,50 +189,71 @@ struct WaveState {
 
 // Per-row constants a pipeline step needs.
 struct RowCtx {
-    const uint16_t *k, *v;
-    const int32_t *tile_valid;
+    const uint16_t *k, *vt;
+    int64_t N;
     int Hkv, kvh, g, qi, wave, lane;
     float scale_log2, lazy_raw;
 };
 
-// S^T for keys 32 kh .. 32 kh + 31 of the K tile in LDS: register i is key
-// 32 kh + 8 (i / 4) + 4 hi + i % 4 of the tile, for query qi.
 template <int D>
-__device__ __forceinline__ f32x16 qk_tile(const WaveState<D> &st, const uint16_t *Kt, const RowCtx &c) {
-    const int l32 = c.lane & 31, hi = c.lane >> 5, kh = c.wave >> 1;
-    const int R = 32 * kh + l32;
-    f32x16 s = f32x16{};
+__device__ __forceinline__ const uint16_t *k_tile_base(const RowCtx &c, int t) {
+    return c.k + (static_cast<int64_t>(t < 0 ? 0 : t) * kTile * c.Hkv + c.kvh) * D;
+}
+template <int D>
+__device__ __forceinline__ const uint16_t *vt_tile_base(const RowCtx &c, int t) {
+    return c.vt + static_cast<int64_t>(c.kvh) * D * c.N + static_cast<int64_t>(t < 0 ? 0 : t) * kTile;
+}
+
+// Operand reads of one step: K(e+1) rows for the scores, V^T(e) rows for the output.
+// Score register i is key 32 kh + 8 (i / 4) + 4 hi + i % 4 of the tile, for query qi.
+template <int D>
+__device__ __forceinline__ void read_k(bf16x8 (&kf)[D / 16], const char *Kt, const RowCtx &c) {
+    const int hi = c.lane >> 5, R = 32 * (c.wave >> 1) + (c.lane & 31);
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Kt + R * D + 8 * k_slot<D>(R, 2 * dc + hi));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[dc], s, 0, 0, 0);
+    for (int dc = 0; dc < D / 16; ++dc)
+        kf[dc] = *reinterpret_cast<const bf16x8 *>(Kt + R * Cfg<D>::KROW + 16 * (2 * dc + hi));
+}
+// A operand of PV K-step j of block db: V^T row 32 db + l32, stored tokens 32 kh + 16 j + 8 hi .. +7
+template <int D>
+__device__ __forceinline__ void read_vt(bf16x8 (&vf)[D / 16], const char *Vt, const RowCtx &c) {
+    const int hi = c.lane >> 5, kh = c.wave >> 1, l32 = c.lane & 31;
+#pragma unroll
+    for (int q = 0; q < D / 16; ++q) {
+        const int d = 32 * (q >> 1) + l32, ch = 4 * kh + 2 * (q & 1) + hi;
+        vf[q] = *reinterpret_cast<const bf16x8 *>(Vt + d * 128 + 16 * vt_slot(d, ch));
     }
-    return s;
+}
+
+template <int D>
+__device__ __forceinline__ void read_vt_half(bf16x8 (&vf)[D / 16], const char *Vt, const RowCtx &c, int half) {
+    const int hi = c.lane >> 5, kh = c.wave >> 1, l32 = c.lane & 31;
+#pragma unroll
+    for (int q = half * (D / 32); q < (half + 1) * (D / 32); ++q) {
+        const int d = 32 * (q >> 1) + l32, ch = 4 * kh + 2 * (q & 1) + hi;
+        vf[q] = *reinterpret_cast<const bf16x8 *>(Vt + d * 128 + 16 * vt_slot(d, ch));
+    }
+}
+
+__device__ __forceinline__ bool needs_mask(int t, int kv_valid, const RowCtx &c) {
+    return kv_valid < kTile || t >= c.g;
 }
 
 // Causal mask on the diagonal tile and padding mask on a partial tile (a select,
-// so NaN in padded K slots never leaks); t < 0 marks a skipped entry.
-__device__ __forceinline__ void mask_tile(f32x16 &s, int t, int kv_valid, const RowCtx &c) {
-    if (kv_valid < kTile || t >= c.g) {
-        const int hi = c.lane >> 5, kh = c.wave >> 1;
-        const int lim = min(kv_valid, c.qi - (t - c.g) * kTile + 1);  // keys < lim survive
+// so NaN in padded K slots never leaks); t < 0 marks a skipped entry (kv_valid 0).
+__device__ __forceinline__ void apply_mask(f32x16 &s, int t, int kv_valid, const RowCtx &c) {
+    const int hi = c.lane >> 5, kh = c.wave >> 1;
+    const int lim = min(kv_valid, c.qi - (t - c.g) * kTile + 1);  // keys < lim survive
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = 32 * kh + 8 * (i >> 2) + 4 * hi + (i & 3);
-            s[i] = key < lim ? s[i] : -INFINITY;
-        }
+    for (int i = 0; i < 16; ++i) {
+        const int key = 32 * kh + 8 * (i >> 2) + 4 * hi + (i & 3);
+        s[i] = key < lim ? s[i] : -INFINITY;
     }
 }
 
-// Online softmax, part 1, run as soon as a tile's (masked) scores exist: tile max,
-// the new reference max -- raised only when the tile exceeds the current one by
-// more than kLazyLog2 in log2 units, decided wave-uniformly -- and, when it moves,
-// the rescale of O and l.  Returns the exp2 bias -m * scale_log2 for part 2.
+// Raise the reference max when the tile's max mt exceeds it by more than kLazyLog2 (decided
+// wave-uniformly), rescaling O and l; returns the exp2 bias -m * scale_log2.
 template <int D>
-__device__ __forceinline__ float softmax_prep(WaveState<D> &st, const f32x16 &s, const RowCtx &c) {
-    float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])), fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
-    mt = pair_max(mt);
+__device__ __forceinline__ float lazy_raise(WaveState<D> &st, float mt, const RowCtx &c) {
     if (__ballot(mt > st.m_run + c.lazy_raw) != 0) {
         const float m_new = fmaxf(st.m_run, mt);
         // m_run = -inf gives exp2(-inf) = 0; both -inf leaves alpha = 1 (O and l are still 0)
@@ -207,12 +266,32 @@ __device__ __forceinline__ float softmax_prep(WaveState<D> &st, const f32x16 &s,
     return (st.m_run == -INFINITY) ? 0.0f : -st.m_run * c.scale_log2;
 }
 
-// Part 2 (branch-free): P = exp2(s * scale_log2 + nbias) rounded to bf16 (the MFMA
-// B operand, two 8-key halves) and l += the sum of the rounded P.
+__device__ __forceinline__ float tile_max(const f32x16 &s) {
+    const float a = max3f(s[0], s[1], s[2]), b = max3f(s[3], s[4], s[5]), d = max3f(s[6], s[7], s[8]);
+    const float e = max3f(a, s[9], s[10]), f = max3f(b, s[11], s[12]), h = max3f(d, s[13], s[14]);
+    return pair_max(max3f(e, f, max3f(h, s[15], s[15])));
+}
+
+// Scores of one K tile (used once per row, for the first listed tile).
 template <int D>
-__device__ __forceinline__ void softmax_exp(WaveState<D> &st, const f32x16 &s, bf16x8 (&pb)[2],
-                                            float nbias, const RowCtx &c) {
+__device__ __forceinline__ f32x16 qk_tile(const WaveState<D> &st, const char *Kt, const RowCtx &c) {
+    bf16x8 kf[D / 16];
+    read_k<D>(kf, Kt, c);
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dc], st.qf[dc], s, 0, 0, 0);
+    return s;
+}
+
+// P = exp2(s * scale_log2 + nbias) rounded to bf16, l += sum of the rounded P, then
+// O += V^T P^T (used once per row, for the last listed tile).
+template <int D>
+__device__ __forceinline__ void exp_pv_tile(WaveState<D> &st, const f32x16 &s, float nbias, const char *Vt,
+                                            const RowCtx &c) {
+    bf16x8 vf[D / 16];
+    read_vt<D>(vf, Vt, c);
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    bf16x8 pb[2];
     float l = st.l_run;
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
@@ -224,273 +303,474 @@ __device__ __forceinline__ void softmax_exp(WaveState<D> &st, const f32x16 &s, b
         pb[i >> 3][(i & 7) + 1] = pr[1];
     }
     st.l_run = l;
+#pragma unroll
+    for (int q = 0; q < D / 16; ++q)
+        st.acc_o[q >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[q], pb[q & 1], st.acc_o[q >> 1], 0, 0, 0);
 }
 
-// O^T += V^T P^T for this wave's 32 keys of the V tile in LDS; K-step j covers
-// keys 32 kh + 16 j + {0..3, 8..11} + 4 hi, read with ds_read_b64_tr_b16.
+// The compute of one pipeline step for listed tile e, whose scores s_cur are formed, masked and
+// prepped (nbias): reads K(e+1) and V^T(e), forms S(e+1) -> s_nxt (masked) interleaved with
+// P(e) = exp2(...), then O += V^T(e) P(e)^T interleaved with the max tree of S(e+1), and the
+// lazy raise for S(e+1) (updates nbias).
 template <int D>
-__device__ __forceinline__ void pv_tile(WaveState<D> &st, const bf16x8 (&pb)[2], const uint16_t *Vt,
-                                        const RowCtx &c) {
-    const int kh = c.wave >> 1, hi = c.lane >> 5;
-    const int s16 = c.lane & 15;
-    const int dsub = 16 * ((c.lane >> 4) & 1);
+__device__ __forceinline__ void step_compute(WaveState<D> &st, const f32x16 &s_cur, f32x16 &s_nxt, float &nbias,
+                                             const char *Kt, const char *Vt, int t_next, int v_next,
+                                             const RowCtx &c) {
+    constexpr int DC = D / 16;
+    constexpr int PAIRS_PER_MFMA = 8 / DC;  // exp pairs issued behind each score MFMA
+    bf16x8 kf[DC], vf[DC];
+    read_k<D>(kf, Kt, c);
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    f32x16 s = f32x16{};
+    bf16x8 pb[2];
+    float l = st.l_run;
+    // software pipeline over the 8 pairs of P(e): fma of pair k + 1 and exp of pair k are
+    // issued while pair k - 1 is rounded and summed, so no VALU op waits on its neighbour
+    float x0 = fmaf(s_cur[0], c.scale_log2, nbias), x1 = fmaf(s_cur[1], c.scale_log2, nbias);
+    float e0 = 0.0f, e1 = 0.0f;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        const int col = 32 * db + dsub + 4 * (s16 & 3);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r0 = 32 * kh + 16 * j + 4 * hi + (s16 >> 2);
-            const int r1 = r0 + 8;
-            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4 *)(Vt + r0 * D + 8 * v_slot<D>(r0, col >> 3) + (col & 7)));
-            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4 *)(Vt + r1 * D + 8 * v_slot<D>(r1, col >> 3) + (col & 7)));
-            const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4, v0),
-                                                     __builtin_bit_cast(bf16x4, v1), 0, 1, 2, 3, 4, 5, 6, 7);
-            st.acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[j], st.acc_o[db], 0, 0, 0);
+    for (int k = 0; k < 8; ++k) {
+        if (k % PAIRS_PER_MFMA == 0) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k / PAIRS_PER_MFMA], st.qf[k / PAIRS_PER_MFMA], s, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (k > 0) {
+            const bf16x2 pr = {static_cast<__bf16>(e0), static_cast<__bf16>(e1)};
+            l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+            pb[(k - 1) >> 2][(2 * (k - 1)) & 7] = pr[0];
+            pb[(k - 1) >> 2][((2 * (k - 1)) & 7) + 1] = pr[1];
+        }
+        e0 = __builtin_amdgcn_exp2f(x0);
+        e1 = __builtin_amdgcn_exp2f(x1);
+        if (k < 7) {
+            x0 = fmaf(s_cur[2 * k + 2], c.scale_log2, nbias);
+            x1 = fmaf(s_cur[2 * k + 3], c.scale_log2, nbias);
+        }
+        // V^T operands in two halves, into the registers the consumed K operands free
+        if (k == 3) read_vt_half<D>(vf, Vt, c, 0);
+        if (k == 5) read_vt_half<D>(vf, Vt, c, 1);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    {
+        const bf16x2 pr = {static_cast<__bf16>(e0), static_cast<__bf16>(e1)};
+        l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+        pb[1][6] = pr[0];
+        pb[1][7] = pr[1];
+    }
+    st.l_run = l;
+    __builtin_amdgcn_sched_barrier(0);
+    // O += V^T(e) P(e)^T, with the max tree of S(e+1) behind the MFMAs (no branch inside this
+    // region: a branch would let the exponentials above sink past the scheduling barriers)
+    float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f;
+#pragma unroll
+    for (int q = 0; q < DC; ++q) {
+        st.acc_o[q >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[q], pb[q & 1], st.acc_o[q >> 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // six max3 steps spread over the DC MFMAs, starting behind the second
+#pragma unroll
+        for (int x = 0; x < 6; ++x) {
+            const int slot = 1 + (x * (DC - 1)) / 6;
+            if (slot != q) continue;
+            if (x == 0) m0 = max3f(s[0], s[1], s[2]);
+            if (x == 1) m1 = max3f(s[3], s[4], s[5]);
+            if (x == 2) m2 = max3f(s[6], s[7], s[8]);
+            if (x == 3) m0 = max3f(m0, s[9], s[10]);
+            if (x == 4) m1 = max3f(m1, s[11], s[12]);
+            if (x == 5) m2 = max3f(m2, s[13], s[14]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    float mt = pair_max(max3f(m0, m1, max3f(m2, s[15], s[15])));
+    if (needs_mask(t_next, v_next, c)) {  // diagonal or partial tile: mask, then max again
+        apply_mask(s, t_next, v_next, c);
+        mt = tile_max(s);
+    }
+    nbias = lazy_raise<D>(st, mt, c);
+    s_nxt = s;
 }
 
-__device__ inline int64_t tile_token(int t) { return static_cast<int64_t>(t < 0 ? 0 : t) * kTile; }
-
-// The row's listed tiles, 64 entries per chunk held across the lanes of two
-// registers (lane j of chunk c: entry 64 c + j, its tile id or -1, and that
-// tile's valid-token count), read with v_readlane.  Vector loads keep these
-// reads out of the scalar/LDS counter, so no per-tile scalar-load latency sits
-// on the critical path; chunk c + 1 is fetched 64 tiles ahead of use.
+// The row's listed tiles, 64 entries per chunk held across the lanes of one register
+// (lane j of chunk c: entry 64 c + j packed as tile id | (valid tokens - 1) << 25, or -1
+// for a skipped entry), read with v_readlane.  Vector loads keep these reads out of the
+// scalar/LDS counter, so no per-tile scalar-load latency sits on the critical path;
+// chunk c + 1 is fetched 64 tiles ahead of use.
 struct TileList {
-    int t0, v0;  // chunk c
-    int t1, v1;  // chunk c + 1
+    int c0, c1;  // chunks c and c + 1
     int c;
 };
 
-__device__ __forceinline__ void fetch_chunk(int &t, int &valid, int base, int n, int e0, int G,
-                                            const int32_t *__restrict__ col_idx,
-                                            const int32_t *__restrict__ tile_valid, int lane) {
+// tile ids of entries [base, base + 64) of a row starting at CSR offset e0 with n entries
+__device__ __forceinline__ int fetch_ids(int base, int n, int e0, int G, const int32_t *__restrict__ col_idx,
+                                         int lane) {
     const int j = base + lane;
-    int x = j < n ? col_idx[e0 + j] : -1;
-    x = (x >= 0 && x < G) ? x : -1;  // out-of-range entries are skipped (masked)
-    t = x;
-    valid = x >= 0 ? tile_valid[x] : 0;
+    const int x = j < n ? col_idx[e0 + j] : -1;
+    return (x >= 0 && x < G) ? x : -1;  // out-of-range entries are skipped (masked)
 }
 
-// Entry i (uniform; c <= i / 64 <= c + 1): tile id and valid count.
+// a tile id packed with its valid-token count (1..64)
+__device__ __forceinline__ int with_valid(int x, const int32_t *__restrict__ tile_valid) {
+    return x >= 0 ? (x | ((tile_valid[x] - 1) << 25)) : -1;
+}
+
+__device__ __forceinline__ int fetch_chunk(int base, int n, int e0, int G, const int32_t *__restrict__ col_idx,
+                                           const int32_t *__restrict__ tile_valid, int lane) {
+    return with_valid(fetch_ids(base, n, e0, G, col_idx, lane), tile_valid);
+}
+
+// Entry i (uniform; c <= i / 64 <= c + 1): tile id (-1: skipped) and valid count (0: skipped).
 __device__ __forceinline__ void list_entry(const TileList &L, int i, int &t, int &valid) {
-    const bool first = (i >> 6) == L.c;
-    t = __builtin_amdgcn_readlane(first ? L.t0 : L.t1, i & 63);
-    valid = __builtin_amdgcn_readlane(first ? L.v0 : L.v1, i & 63);
+    const int p = __builtin_amdgcn_readlane((i >> 6) == L.c ? L.c0 : L.c1, i & 63);
+    t = p < 0 ? -1 : (p & 0x1FFFFFF);
+    valid = p < 0 ? 0 : (p >> 25) + 1;
 }
 
-// One pipeline step for listed tile e (scores s_cur formed, masked and prepped):
-//   wait + barrier; start K(e+2) -> k_free and V(e+1) -> v_free;
-//   S(e+1) = K(e+1) Q^T from k_next interleaved with P(e) = exp2(...) of S(e);
-//   O += V(e) P(e) from v_cur; mask and prep S(e+1).
-template <int D>
-__device__ __forceinline__ void pipe_step(WaveState<D> &st, f32x16 &s_cur, float &nbias,
-                                          const uint16_t *k_next, const uint16_t *v_cur,
-                                          uint16_t *k_free, uint16_t *v_free, int t_next, int v_next,
-                                          int t_next2, bool has_next2, const LoadOffsets<D> &off,
-                                          const RowCtx &c) {
-    wait_vmcnt_le(0);
-    __builtin_amdgcn_s_barrier();  // K(e+1), V(e) landed; everyone left step e-1
-    if (has_next2) load_half<D>(c.k, tile_token(t_next2), c.Hkv, c.kvh, k_free, c.wave, off.k);
-    load_half<D>(c.v, tile_token(t_next), c.Hkv, c.kvh, v_free, c.wave, off.v);
-    // one scheduling region: the MFMA chain of S(e+1) interleaved with P(e)
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 s_nxt = qk_tile<D>(st, k_next, c);
-    bf16x8 pb[2];
-    softmax_exp<D>(st, s_cur, pb, nbias, c);
-#pragma unroll
-    for (int x = 0; x < D / 16; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // then VALU + transcendental work
+__device__ __forceinline__ void advance_chunk(TileList &L, int i, int n, int e0, int G,
+                                              const int32_t *__restrict__ col_idx,
+                                              const int32_t *__restrict__ tile_valid, int lane) {
+    if ((i >> 6) != L.c) {  // entry i entered chunk c + 1: shift, fetch chunk c + 2
+        L.c += 1;
+        L.c0 = L.c1;
+        L.c1 = fetch_chunk(64 * (L.c + 1), n, e0, G, col_idx, tile_valid, lane);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    pv_tile<D>(st, pb, v_cur, c);
-    mask_tile(s_nxt, t_next, v_next, c);
-    nbias = softmax_prep<D>(st, s_nxt, c);
-    s_cur = s_nxt;
 }
 
+// A zero the compiler cannot see through: per-row values derived from it are recomputed for
+// every row instead of being kept live (in registers) across the output merge.
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+
+// Workgroup barrier that orders LDS accesses only: in-flight global loads and stores stay in
+// flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// A CSR row: q head h, query tile g, read KV head kvh; rows are numbered KV-head-major,
+// latest query tile first.
+struct RowId {
+    int kvh, g, h;
+};
+__device__ __forceinline__ RowId row_of(int idx, int G, int group) {
+    const int kvh = idx / (G * group), rem = idx % (G * group);
+    return RowId{kvh, G - 1 - rem / group, kvh * group + rem % group};
+}
+
+template <int D>
+__device__ __forceinline__ void load_q(WaveState<D> &st, const uint16_t *__restrict__ q, const RowId &r, int Hq,
+                                       int qi, int hi) {
+    const uint16_t *qrow = q + ((static_cast<int64_t>(r.g) * kTile + qi) * Hq + r.h) * D + 8 * hi;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc)  // read once: stream it past L2 (keep L2 for K/V tiles)
+        st.qf[dc] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(qrow + 16 * dc));
+}
+
+// Row queues, one per XCD, over the KV-head-major row order, so that the workgroups of one
+// XCD (one L2) work on one KV head at a time:
+//   mode 0 (Hkv divides 8): the 8 / Hkv XCDs of a KV head take its rows interleaved;
+//   mode 1 (8 divides Hkv): XCD x takes KV heads x, x + 8, ... in turn;
+//   mode 2 (otherwise): XCD x takes the x-th contiguous eighth of the order.
+// Within a KV head rows run latest query tile first, i.e. longest rows first.
+struct Queues {
+    int mode, xpk, Rh, rpx, nrows, Hkv;
+};
+
+__device__ inline int queue_len(const Queues &Q, int x) {
+    if (Q.mode == 0) {
+        const int sub = x % Q.xpk;
+        return Q.Rh > sub ? (Q.Rh - sub + Q.xpk - 1) / Q.xpk : 0;
+    }
+    if (Q.mode == 1) return (Q.Hkv / kXcds) * Q.Rh;
+    const int b = x * Q.rpx;
+    return max(0, min(Q.nrows, b + Q.rpx) - b);
+}
+
+__device__ inline int queue_row(const Queues &Q, int x, int pos) {
+    if (Q.mode == 0) return (x / Q.xpk) * Q.Rh + x % Q.xpk + pos * Q.xpk;
+    if (Q.mode == 1) return (x + kXcds * (pos / Q.Rh)) * Q.Rh + pos % Q.Rh;
+    return x * Q.rpx + pos;
+}
+
+// Resolve a claimed position of queue q % 8 into a row; when that queue is exhausted, claim
+// from the following queues in turn (a workgroup whose own XCD is done helps the others).
+// Returns -1 once all eight are exhausted.  One lane runs it.
+__device__ inline int resolve_claim(int *__restrict__ counters, const Queues &Q, int &q, int home, int pos) {
+    while (true) {
+        if (pos < queue_len(Q, q % kXcds)) return queue_row(Q, q % kXcds, pos);
+        if (++q >= home + kXcds) return -1;
+        pos = atomicAdd(&counters[q % kXcds], 1);
+    }
+}
+
+// Persistent, two workgroups per CU.  Workgroup b runs on XCD b % 8 and claims rows from that
+// XCD's queue with an atomic counter (zeroed by the V transpose that precedes this kernel),
+// so rows are balanced dynamically, longest first.  The next row is claimed at the start of
+// the current one; its Q, CSR offsets and first list chunk are fetched while the current row
+// finishes (its last tile and the output merge).
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_prefill_kernel(
     PlanView pv, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, const int32_t *__restrict__ row_ptr,
+    const uint16_t *__restrict__ vt, const int32_t *__restrict__ row_ptr,
     const int32_t *__restrict__ col_idx, float scale, float scale_log2, float lazy_raw,
-    float *__restrict__ out, float *__restrict__ lse, int Hq, int Hkv, int rows_per_xcd) {
+    float *__restrict__ out, float *__restrict__ lse, int Hq, int Hkv, Queues Qs, int *__restrict__ counters) {
     using C = Cfg<D>;
-    constexpr int DC = D / 16;
     constexpr int DB = D / 32;
     // four separate tile buffers, so that each LDS read has one known underlying object
-    __shared__ __attribute__((aligned(16))) uint16_t kb0[C::TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t kb1[C::TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t vb0[C::TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t vb1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char kb0[C::KBYTES];
+    __shared__ __attribute__((aligned(1024))) char kb1[C::KBYTES];
+    __shared__ __attribute__((aligned(1024))) char vb0[C::VBYTES];
+    __shared__ __attribute__((aligned(1024))) char vb1[C::VBYTES];
+    __shared__ int s_row;  // the row wave 0 claimed for the workgroup
 
     if (!plan_ok(pv)) return;
     const int G = pv.num_tiles;
-    const int nrows = Hq * G;
-    // workgroup -> row: XCD x (= blockIdx % 8) owns a contiguous share of the
-    // KV-head-major, latest-tile-first row order
-    const int idx = (blockIdx.x % kXcds) * rows_per_xcd + blockIdx.x / kXcds;
-    if (idx >= nrows) return;
     const int group = Hq / Hkv;
-    const int kvh = idx / (G * group);
-    const int rem = idx % (G * group);
-    const int g = G - 1 - rem / group;
-    const int h = kvh * group + rem % group;
-    const int64_t row = static_cast<int64_t>(h) * G + g;
     const int64_t N = static_cast<int64_t>(G) * kTile;
+    const int home = blockIdx.x % kXcds;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wavefront
-    const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
     const int qh = wave & 1, kh = wave >> 1;
-    const int qi = 32 * qh + l32;  // this lane's query in the tile
-    const int q_valid = uniform_read(pv.tile_valid, g);
-    const int64_t tok0 = static_cast<int64_t>(g) * kTile;
-    const LoadOffsets<D> off = make_load_offsets<D>(Hkv, wave, lane);
-    const RowCtx ctx{k, v, pv.tile_valid, Hkv, kvh, g, qi, wave, lane, scale_log2, lazy_raw};
+    int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    int qi = 32 * qh + l32;  // this lane's query in the tile
+    const bool claimer = tid == 0;
+    int cq = home;  // claimer: the queue it draws from
 
+    if (claimer) s_row = resolve_claim(counters, Qs, cq, home, atomicAdd(&counters[home], 1));
+    lds_barrier();
+    int row_idx = s_row;
+    if (row_idx < 0) return;
+
+    // the first row's Q, CSR offsets and first list chunk
+    RowId rid = row_of(row_idx, G, group);
     WaveState<D> st;
+    load_q<D>(st, q, rid, Hq, qi, hi);
+    int e0, n;
     {
-        const uint16_t *qrow = q + ((tok0 + qi) * Hq + h) * D + 8 * hi;
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc)  // read once: stream it past L2 (keep L2 for K/V tiles)
-            st.qf[dc] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(qrow + 16 * dc));
+        const int64_t row = static_cast<int64_t>(rid.h) * G + rid.g;
+        e0 = uniform_read(row_ptr, row);
+        n = uniform_read(row_ptr, row + 1) - e0;
     }
-#pragma unroll
-    for (int db = 0; db < DB; ++db) st.acc_o[db] = f32x16{};
-    st.m_run = -INFINITY;
-    st.l_run = 0.0f;
+    int ids0 = fetch_ids(0, n, e0, G, col_idx, lane);  // tile ids of the row's entries 0..63
 
-    const int e0 = uniform_read(row_ptr, row), e1 = uniform_read(row_ptr, row + 1);
-    const int n = e1 - e0;
-    if (n > 0) {
-        TileList L;
-        L.c = 0;
-        fetch_chunk(L.t0, L.v0, 0, n, e0, G, col_idx, pv.tile_valid, lane);
-        fetch_chunk(L.t1, L.v1, 64, n, e0, G, col_idx, pv.tile_valid, lane);
-        int t0, v0, t1, v1;
-        list_entry(L, 0, t0, v0);
-        list_entry(L, 1, t1, v1);  // entry n: t = -1 when past the end
-        // prologue: K(0), V(0), K(1) in flight; S(0) formed, masked, prepped
-        load_half<D>(k, tile_token(t0), Hkv, kvh, kb0, wave, off.k);
-        load_half<D>(v, tile_token(t0), Hkv, kvh, vb0, wave, off.v);
-        if (n > 1) load_half<D>(k, tile_token(t1), Hkv, kvh, kb1, wave, off.k);
-        wait_vmcnt_le(0);
-        __builtin_amdgcn_s_barrier();
-        f32x16 s_cur = qk_tile<D>(st, kb0, ctx);
-        mask_tile(s_cur, t0, v0, ctx);
-        float nbias = softmax_prep<D>(st, s_cur, ctx);
-        // steady state, unrolled by two so every buffer has a fixed role
-        int i = 0;
-        int t_a = t1, v_a = v1;  // entry i + 1
-        while (i + 1 < n) {
-            if ((i >> 6) != L.c) {  // entry i entered chunk c + 1: shift, fetch chunk c + 2
-                L.c += 1;
-                L.t0 = L.t1;
-                L.v0 = L.v1;
-                fetch_chunk(L.t1, L.v1, 64 * (L.c + 1), n, e0, G, col_idx, pv.tile_valid, lane);
-            }
-            int t_b, v_b;
-            list_entry(L, i + 2, t_b, v_b);
-            pipe_step<D>(st, s_cur, nbias, kb1, vb0, kb0, vb1, t_a, v_a, t_b, i + 2 < n, off, ctx);
-            ++i;
-            if (i + 1 >= n) break;
-            if ((i >> 6) != L.c) {
-                L.c += 1;
-                L.t0 = L.t1;
-                L.v0 = L.v1;
-                fetch_chunk(L.t1, L.v1, 64 * (L.c + 1), n, e0, G, col_idx, pv.tile_valid, lane);
-            }
-            t_a = t_b;
-            v_a = v_b;
-            list_entry(L, i + 2, t_b, v_b);
-            pipe_step<D>(st, s_cur, nbias, kb0, vb1, kb1, vb0, t_a, v_a, t_b, i + 2 < n, off, ctx);
-            ++i;
-            t_a = t_b;
-            v_a = v_b;
-        }
-        // last listed tile: softmax + PV only (its V is in vb[i % 2])
-        wait_vmcnt_le(0);
-        __builtin_amdgcn_s_barrier();
-        bf16x8 pb[2];
-        softmax_exp<D>(st, s_cur, pb, nbias, ctx);
-        if ((i & 1) == 0) pv_tile<D>(st, pb, vb0, ctx);
-        else pv_tile<D>(st, pb, vb1, ctx);
-    }
+    while (true) {
+        lane = (tid & 63) + opaque_zero();
+        l32 = lane & 31;
+        hi = lane >> 5;
+        qi = 32 * qh + l32;
+        const LoadOffsets<D> off = make_load_offsets<D>(Hkv, N, wave, lane);
+        const int g = rid.g, h = rid.h;
+        const int64_t tok0 = static_cast<int64_t>(g) * kTile;
+        const int q_valid = uniform_read(pv.tile_valid, g);
+        const RowCtx ctx{k, vt, N, Hkv, rid.kvh, g, qi, wave, lane, scale_log2, lazy_raw};
+#pragma unroll
+        for (int db = 0; db < DB; ++db) st.acc_o[db] = f32x16{};
+        st.m_run = -INFINITY;
+        st.l_run = 0.0f;
 
-    // merge the two key halves: waves with kh = 1 publish, waves with kh = 0 combine
-    const float l_tot = pair_sum(st.l_run);
-    float *X = reinterpret_cast<float *>(kb0);  // [D/2 registers][2 query halves][64 lanes] (kb0 + kb1)
-    float *ML = reinterpret_cast<float *>(vb0);  // [2 query halves][32 queries][m, l]
-    __syncthreads();
-    if (kh == 1) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = db * 16 + i;  // first D/4 registers in kb0, the rest in kb1
-                float *dst = r < D / 4 ? X : reinterpret_cast<float *>(kb1);
-                dst[(((r % (D / 4)) * 2) + qh) * 64 + lane] = st.acc_o[db][i];
+        // claim the next row now; the claim resolves at this row's last tile
+        int claim = 0;
+        if (claimer) claim = atomicAdd(&counters[cq % kXcds], 1);
+        int nptr = 0;  // lane 0: next row's first CSR offset, lane 1: its end
+        int next_idx = -1;
+        // publish the claimed row (claimer), then every wave starts fetching it
+        auto resolve_next = [&]() {
+            if (claimer) s_row = resolve_claim(counters, Qs, cq, home, claim);
+            lds_barrier();
+            next_idx = s_row;
+        };
+        auto prefetch_next = [&]() {
+            if (next_idx >= 0) {
+                const RowId nid = row_of(next_idx, G, group);
+                load_q<D>(st, q, nid, Hq, qi, hi);
+                nptr = row_ptr[static_cast<int64_t>(nid.h) * G + nid.g + (lane & 1)];
             }
-        if (hi == 0) {
-            ML[(qh * 32 + l32) * 2 + 0] = st.m_run;
-            ML[(qh * 32 + l32) * 2 + 1] = l_tot;
+        };
+
+        if (n > 0) {
+            // prologue: K(0), V(0), K(1) in flight (their tile ids straight from the id chunk), then
+            // the valid counts of the list; S(0) formed, masked, prepped
+            {
+                const int i0 = __builtin_amdgcn_readlane(ids0, 0), i1 = __builtin_amdgcn_readlane(ids0, 1);
+                load_k_tile<D>(k_tile_base<D>(ctx, i0), kb0, wave, off.k);
+                load_vt_tile<D>(vt_tile_base<D>(ctx, i0), vb0, wave, off.v);
+                if (n > 1) load_k_tile<D>(k_tile_base<D>(ctx, i1), kb1, wave, off.k);
+            }
+            TileList L;
+            L.c = 0;
+            L.c0 = with_valid(ids0, pv.tile_valid);
+            L.c1 = n > 64 ? fetch_chunk(64, n, e0, G, col_idx, pv.tile_valid, lane) : -1;
+            int t0, v0, t1, v1;
+            list_entry(L, 0, t0, v0);
+            list_entry(L, 1, t1, v1);  // entry n: t = -1 when past the end
+            wait_vmcnt_le(0);
+            __builtin_amdgcn_s_barrier();
+            f32x16 sa = qk_tile<D>(st, kb0, ctx), sb;
+            if (needs_mask(t0, v0, ctx)) apply_mask(sa, t0, v0, ctx);
+            float nbias = lazy_raise<D>(st, tile_max(sa), ctx);
+            // steady state, unrolled by two so that every buffer and score register has a fixed
+            // role: step e: wait + barrier; K(e+2) -> free K buffer, V(e+1) -> free V buffer; compute
+            int i = 0;
+            int t_a = t1, v_a = v1;  // entry i + 1
+            while (i + 1 < n) {
+                advance_chunk(L, i, n, e0, G, col_idx, pv.tile_valid, lane);
+                int t_b, v_b;
+                list_entry(L, i + 2, t_b, v_b);
+                wait_vmcnt_le(0);
+                __builtin_amdgcn_s_barrier();  // K(e+1), V(e) landed; everyone left step e-1
+                if (i + 2 < n) load_k_tile<D>(k_tile_base<D>(ctx, t_b), kb0, wave, off.k);
+                load_vt_tile<D>(vt_tile_base<D>(ctx, t_a), vb1, wave, off.v);
+                __builtin_amdgcn_sched_barrier(0);
+                step_compute<D>(st, sa, sb, nbias, kb1, vb0, t_a, v_a, ctx);
+                ++i;
+                t_a = t_b;
+                v_a = v_b;
+                if (i + 1 >= n) break;
+                advance_chunk(L, i, n, e0, G, col_idx, pv.tile_valid, lane);
+                list_entry(L, i + 2, t_b, v_b);
+                wait_vmcnt_le(0);
+                __builtin_amdgcn_s_barrier();
+                if (i + 2 < n) load_k_tile<D>(k_tile_base<D>(ctx, t_b), kb1, wave, off.k);
+                load_vt_tile<D>(vt_tile_base<D>(ctx, t_a), vb0, wave, off.v);
+                __builtin_amdgcn_sched_barrier(0);
+                step_compute<D>(st, sb, sa, nbias, kb0, vb1, t_a, v_a, ctx);
+                ++i;
+                t_a = t_b;
+                v_a = v_b;
+            }
+            // last listed tile: softmax + PV only (its scores in sa for even i, its V^T in vb[i % 2]);
+            // Q is no longer needed, so the next row's Q and CSR offsets start loading now
+            wait_vmcnt_le(0);
+            resolve_next();
+            prefetch_next();
+            if ((i & 1) == 0) exp_pv_tile<D>(st, sa, nbias, vb0, ctx);
+            else exp_pv_tile<D>(st, sb, nbias, vb1, ctx);
+        } else {
+            resolve_next();
+            prefetch_next();
         }
-    }
-    __syncthreads();
-    float m_fin = -INFINITY, l_fin = 0.0f;
-    if (kh == 0) {
-        const float m1 = ML[(qh * 32 + l32) * 2 + 0];
-        const float l1 = ML[(qh * 32 + l32) * 2 + 1];
-        m_fin = fmaxf(st.m_run, m1);
-        const float a0 = (st.m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((st.m_run - m_fin) * scale_log2);
-        const float a1 = (m1 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m1 - m_fin) * scale_log2);
-        l_fin = l_tot * a0 + l1 * a1;
-        const float inv = l_fin > 0.0f ? 1.0f / l_fin : 0.0f;
-        const float w0 = a0 * inv, w1 = a1 * inv;
+
+        // merge the two key halves: waves with kh = 1 publish, waves with kh = 0 combine
+        const float l_tot = pair_sum(st.l_run);
+        float *X = reinterpret_cast<float *>(kb0);  // [D/2 registers][2 query halves][64 lanes] (kb0 + kb1)
+        float *ML = reinterpret_cast<float *>(vb0);  // [2 query halves][32 queries][m, l]
+        lds_barrier();
+        if (kh == 1) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = db * 16 + i;
-                const float *src = r < D / 4 ? X : reinterpret_cast<const float *>(kb1);
-                st.acc_o[db][i] = st.acc_o[db][i] * w0 + src[(((r % (D / 4)) * 2) + qh) * 64 + lane] * w1;
+                for (int i = 0; i < 16; ++i) {
+                    const int r = db * 16 + i;  // first D/4 registers in kb0, the rest in kb1
+                    float *dst = r < D / 4 ? X : reinterpret_cast<float *>(kb1);
+                    dst[(((r % (D / 4)) * 2) + qh) * 64 + lane] = st.acc_o[db][i];
+                }
+            if (hi == 0) {
+                ML[(qh * 32 + l32) * 2 + 0] = st.m_run;
+                ML[(qh * 32 + l32) * 2 + 1] = l_tot;
             }
-    }
-    __syncthreads();
-    // output tile staged in kb0|kb1 as [64 rows][D/4 float4 chunks], chunk c of row r at c ^ (r % 32);
-    // rows 0..31 in kb0, rows 32..63 in kb1
-    constexpr int C4 = D / 4;
-    auto orow = [&](int r) -> float * {
-        return reinterpret_cast<float *>(r < 32 ? kb0 : kb1) + (r & 31) * D;
-    };
-    if (kh == 0) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const f32x4 o4 = {st.acc_o[db][4 * i4 + 0], st.acc_o[db][4 * i4 + 1],
-                                  st.acc_o[db][4 * i4 + 2], st.acc_o[db][4 * i4 + 3]};
-                const int c4 = 8 * db + 2 * i4 + hi;
-                *reinterpret_cast<f32x4 *>(orow(qi) + 4 * (c4 ^ (qi & (C4 - 1)))) = o4;
-            }
-        if (lse != nullptr && hi == 0) {
-            const bool live = qi < q_valid && l_fin > 0.0f;
-            lse[static_cast<int64_t>(h) * N + tok0 + qi] = live ? m_fin * scale + logf(l_fin) : -INFINITY;
         }
+        lds_barrier();
+        float m_fin = -INFINITY, l_fin = 0.0f;
+        if (kh == 0) {
+            const float m1 = ML[(qh * 32 + l32) * 2 + 0];
+            const float l1 = ML[(qh * 32 + l32) * 2 + 1];
+            m_fin = fmaxf(st.m_run, m1);
+            const float a0 = (st.m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((st.m_run - m_fin) * scale_log2);
+            const float a1 = (m1 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m1 - m_fin) * scale_log2);
+            l_fin = l_tot * a0 + l1 * a1;
+            const float inv = l_fin > 0.0f ? 1.0f / l_fin : 0.0f;
+            const float w0 = a0 * inv, w1 = a1 * inv;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = db * 16 + i;
+                    const float *src = r < D / 4 ? X : reinterpret_cast<const float *>(kb1);
+                    st.acc_o[db][i] = st.acc_o[db][i] * w0 + src[(((r % (D / 4)) * 2) + qh) * 64 + lane] * w1;
+                }
+        }
+        // the next row's first list chunk: its tile ids now, their valid counts after the stores
+        const bool has_next = next_idx >= 0;
+        int e0n = 0, nn = 0, ids = -1;
+        if (has_next) {
+            e0n = __builtin_amdgcn_readlane(nptr, 0);
+            nn = __builtin_amdgcn_readlane(nptr, 1) - e0n;
+            ids = fetch_ids(0, nn, e0n, G, col_idx, lane);
+        }
+        lds_barrier();
+        // output tile staged in kb0|kb1 as [64 rows][D/4 float4 chunks], chunk c of row r at
+        // c ^ (r % 32); rows 0..31 in kb0, rows 32..63 in kb1
+        constexpr int C4 = D / 4;
+        auto orow = [&](int r) -> float * {
+            return reinterpret_cast<float *>(r < 32 ? kb0 : kb1) + (r & 31) * D;
+        };
+        if (kh == 0) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x4 o4 = {st.acc_o[db][4 * i4 + 0], st.acc_o[db][4 * i4 + 1],
+                                      st.acc_o[db][4 * i4 + 2], st.acc_o[db][4 * i4 + 3]};
+                    const int c4 = 8 * db + 2 * i4 + hi;
+                    *reinterpret_cast<f32x4 *>(orow(qi) + 4 * (c4 ^ (qi & (C4 - 1)))) = o4;
+                }
+            if (lse != nullptr && hi == 0) {
+                const bool live = qi < q_valid && l_fin > 0.0f;
+                lse[static_cast<int64_t>(h) * N + tok0 + qi] = live ? m_fin * scale + logf(l_fin) : -INFINITY;
+            }
+        }
+        lds_barrier();
+        for (int x = tid; x < 64 * C4; x += kThreads) {
+            const int r = x / C4, c4 = x % C4;
+            f32x4 val = *reinterpret_cast<const f32x4 *>(orow(r) + 4 * (c4 ^ (r & (C4 - 1))));
+            if (r >= q_valid) val = f32x4{};
+            // written once: non-temporal, so 32 KB of output per row does not evict K/V tiles
+            __builtin_nontemporal_store(val, reinterpret_cast<f32x4 *>(out + ((tok0 + r) * Hq + h) * D + 4 * c4));
+        }
+        if (!has_next) break;
+        ids0 = ids;
+        lds_barrier();  // every wave has read the staged output before the next row's tiles land
+        rid = row_of(next_idx, G, group);
+        e0 = e0n;
+        n = nn;
+    }
+}
+
+// V [N][Hkv][D] (bf16 or fp32, rounded to bf16) -> V^T [Hkv][D][N] with the tokens of every
+// 16-token group at vt_pos.  One workgroup per (64-token tile, kv head): the tile goes through
+// LDS so that both the 2D-byte row reads and the 128-byte V^T row writes are whole rows.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const T *__restrict__ v, uint16_t *__restrict__ vt,
+                                                          int Hkv, int64_t N, int *__restrict__ counters) {
+    // the attention kernel that follows on the stream claims rows from these counters
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kXcds) counters[threadIdx.x] = 0;
+    constexpr int LD = D + 2;  // padded LDS row (bf16 elements): column reads hit distinct banks
+    __shared__ uint16_t tile[64 * LD];
+    const int t = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
+    const int64_t tok0 = static_cast<int64_t>(t) * kTile;
+    for (int x = tid; x < 64 * D; x += 256) {
+        const int r = x / D, d = x % D;
+        const T val = v[((tok0 + r) * Hkv + kvh) * D + d];
+        tile[r * LD + d] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));
     }
     __syncthreads();
-    for (int x = tid; x < 64 * C4; x += kThreads) {
-        const int r = x / C4, c4 = x % C4;
-        f32x4 val = *reinterpret_cast<const f32x4 *>(orow(r) + 4 * (c4 ^ (r & (C4 - 1))));
-        if (r >= q_valid) val = f32x4{};
-        // written once: non-temporal, so 32 KB of output per row does not evict K/V tiles
-        __builtin_nontemporal_store(val, reinterpret_cast<f32x4 *>(out + ((tok0 + r) * Hq + h) * D + 4 * c4));
+    // V^T row d of this tile: 64 stored positions; thread writes 8 consecutive positions
+    for (int x = tid; x < D * 8; x += 256) {
+        const int d = x / 8, c = x % 8;
+        uint16_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = tile[static_cast<int>(vt_pos(8 * c + j)) * LD + d];
+        uint4 pk;
+        pk.x = w[0] | (uint32_t(w[1]) << 16);
+        pk.y = w[2] | (uint32_t(w[3]) << 16);
+        pk.z = w[4] | (uint32_t(w[5]) << 16);
+        pk.w = w[6] | (uint32_t(w[7]) << 16);
+        *reinterpret_cast<uint4 *>(vt + (static_cast<int64_t>(kvh) * D + d) * N + tok0 + 8 * c) = pk;
     }
 }
 
@@ -510,24 +790,51 @@ hipError_t launch_cast_bf16(const float *src, uint16_t *dst, int64_t n, hipStrea
     return hipGetLastError();
 }
 
+hipError_t launch_transpose_v(const HostLayout &hl, const void *v, bool fp32, uint16_t *vt, int *counters,
+                              hipStream_t stream) {
+    if (hl.G == 0) return hipSuccess;
+    const int64_t N = int64_t(hl.G) * kTile;
+    const dim3 grid(static_cast<unsigned>(hl.G), static_cast<unsigned>(hl.Hkv));
+    if (hl.D == 128) {
+        if (fp32) transpose_v_kernel<128, float><<<grid, 256, 0, stream>>>(static_cast<const float *>(v), vt, hl.Hkv, N, counters);
+        else transpose_v_kernel<128, __bf16><<<grid, 256, 0, stream>>>(static_cast<const __bf16 *>(v), vt, hl.Hkv, N, counters);
+    } else {
+        if (fp32) transpose_v_kernel<64, float><<<grid, 256, 0, stream>>>(static_cast<const float *>(v), vt, hl.Hkv, N, counters);
+        else transpose_v_kernel<64, __bf16><<<grid, 256, 0, stream>>>(static_cast<const __bf16 *>(v), vt, hl.Hkv, N, counters);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill(const HostLayout &hl, const PlanView &pv, const uint16_t *q,
-                          const uint16_t *k, const uint16_t *v, const int32_t *row_ptr,
-                          const int32_t *col_idx, float scale, float *out, float *lse,
+                          const uint16_t *k, const uint16_t *vt, const int32_t *row_ptr,
+                          const int32_t *col_idx, float scale, float *out, float *lse, int *counters,
                           hipStream_t stream) {
     const int64_t rows = int64_t(hl.Hq) * hl.G;
     if (rows == 0) return hipSuccess;
     const float scale_log2 = scale * 1.4426950408889634f;
     const float lazy_raw = kLazyLog2 / scale_log2;
-    const int rows_per_xcd = static_cast<int>((rows + kXcds - 1) / kXcds);
-    const unsigned grid = static_cast<unsigned>(rows_per_xcd) * kXcds;
+    Queues Qs{};
+    Qs.nrows = static_cast<int>(rows);
+    Qs.Hkv = hl.Hkv;
+    Qs.Rh = static_cast<int>(rows / hl.Hkv);
+    Qs.rpx = static_cast<int>((rows + kXcds - 1) / kXcds);
+    if (kXcds % hl.Hkv == 0) {
+        Qs.mode = 0;
+        Qs.xpk = kXcds / hl.Hkv;
+    } else if (hl.Hkv % kXcds == 0) {
+        Qs.mode = 1;
+    } else {
+        Qs.mode = 2;
+    }
+    // persistent: two workgroups per CU (256 CUs), never more workgroups than rows
+    const int per_xcd = static_cast<int>(std::min<int64_t>((rows + kXcds - 1) / kXcds, kPersistentPerXcd));
+    const unsigned grid = static_cast<unsigned>(per_xcd) * kXcds;
     if (hl.D == 128)
         sparse_prefill_kernel<128><<<grid, kThreads, 0, stream>>>(
-            pv, q, k, v, row_ptr, col_idx, scale, scale_log2, lazy_raw, out, lse, hl.Hq, hl.Hkv,
-            rows_per_xcd);
+            pv, q, k, vt, row_ptr, col_idx, scale, scale_log2, lazy_raw, out, lse, hl.Hq, hl.Hkv, Qs, counters);
     else
         sparse_prefill_kernel<64><<<grid, kThreads, 0, stream>>>(
-            pv, q, k, v, row_ptr, col_idx, scale, scale_log2, lazy_raw, out, lse, hl.Hq, hl.Hkv,
-            rows_per_xcd);
+            pv, q, k, vt, row_ptr, col_idx, scale, scale_log2, lazy_raw, out, lse, hl.Hq, hl.Hkv, Qs, counters);
     return hipGetLastError();
 }
 

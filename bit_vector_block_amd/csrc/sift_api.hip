@@ -71,9 +71,11 @@ sift_status build_layout(const sift_layout *layout, HostLayout *out) {
         }
     }
     max_nnz *= L.num_q_heads;
-    // Token indices, CSR entries and word offsets are int32 on the device.
+    // Token indices, CSR entries and word offsets are int32 on the device; a lane's offset into
+    // V^T (row d of D, 2 N bytes per row) is uint32.
     if (G * kTile > kInt32Max || G * L.num_q_heads >= kInt32Max || max_nnz >= kInt32Max ||
-        la_words > kInt32Max || ca_words > kInt32Max)
+        la_words > kInt32Max || ca_words > kInt32Max ||
+        G * kTile * 2 * static_cast<int64_t>(L.head_dim) > 2 * kInt32Max)
         return SIFT_ERR_UNSUPPORTED;
     hl.G = static_cast<int32_t>(G);
     hl.la_words = la_words;
@@ -183,10 +185,14 @@ size_t decode_workspace_bytes(const HostLayout &hl) {
            align256(sizeof(int32_t) * size_t(hl.Hq));
 }
 
+// Prefill scratch: 256 bytes of row-queue counters, V^T (bf16 [Hkv][D][N]); for SIFT_FP32
+// inputs the bf16 copies of Q and K follow.
+constexpr size_t kCounterBytes = 256;
 static size_t prefill_workspace_bytes(const HostLayout &hl, sift_dtype dtype) {
-    if (dtype != SIFT_FP32) return 0;
     const size_t N = size_t(hl.G) * kTile;
-    return align256(2 * N * hl.Hq * hl.D) + 2 * align256(2 * N * hl.Hkv * hl.D);
+    const size_t vt = kCounterBytes + align256(2 * N * hl.Hkv * hl.D);
+    if (dtype != SIFT_FP32) return vt;
+    return vt + align256(2 * N * hl.Hq * hl.D) + align256(2 * N * hl.Hkv * hl.D);
 }
 
 }  // namespace sift
@@ -298,28 +304,27 @@ sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan, c
     if (!(scale > 0.0f)) scale = 1.0f / sqrtf(float(hl.D));
     if (!isfinite(scale)) return SIFT_ERR_INVALID;
     const size_t need = prefill_workspace_bytes(hl, dtype);
-    if (need > 0 && (!d_workspace || workspace_bytes < need)) return SIFT_ERR_CAPACITY;
+    if (!d_workspace || workspace_bytes < need) return SIFT_ERR_CAPACITY;
     const PlanView pv = plan_view(hl, d_plan);
     const uint16_t *q = static_cast<const uint16_t *>(d_q);
     const uint16_t *k = static_cast<const uint16_t *>(d_k);
-    const uint16_t *v = static_cast<const uint16_t *>(d_v);
+    const int64_t N = int64_t(hl.G) * kTile;
+    const int64_t nq = N * hl.Hq * hl.D, nkv = N * hl.Hkv * hl.D;
+    char *ws = static_cast<char *>(d_workspace);
+    int *counters = reinterpret_cast<int *>(ws);
+    uint16_t *vt = reinterpret_cast<uint16_t *>(ws + kCounterBytes);
     if (dtype == SIFT_FP32) {
-        const int64_t N = int64_t(hl.G) * kTile;
-        const int64_t nq = N * hl.Hq * hl.D, nkv = N * hl.Hkv * hl.D;
-        char *ws = static_cast<char *>(d_workspace);
-        uint16_t *qb = reinterpret_cast<uint16_t *>(ws);
-        uint16_t *kb = reinterpret_cast<uint16_t *>(ws + align256(2 * size_t(nq)));
-        uint16_t *vb = reinterpret_cast<uint16_t *>(ws + align256(2 * size_t(nq)) + align256(2 * size_t(nkv)));
+        char *ws2 = ws + kCounterBytes + align256(2 * size_t(nkv));
+        uint16_t *qb = reinterpret_cast<uint16_t *>(ws2);
+        uint16_t *kb = reinterpret_cast<uint16_t *>(ws2 + align256(2 * size_t(nq)));
         if (launch_cast_bf16(static_cast<const float *>(d_q), qb, nq, stream) != hipSuccess ||
-            launch_cast_bf16(static_cast<const float *>(d_k), kb, nkv, stream) != hipSuccess ||
-            launch_cast_bf16(static_cast<const float *>(d_v), vb, nkv, stream) != hipSuccess)
+            launch_cast_bf16(static_cast<const float *>(d_k), kb, nkv, stream) != hipSuccess)
             return SIFT_ERR_HIP;
         q = qb;
         k = kb;
-        v = vb;
     }
-    if (launch_prefill(hl, pv, q, k, v, d_row_ptr, d_col_idx, scale, d_out, d_lse, stream) !=
-        hipSuccess)
+    if (launch_transpose_v(hl, d_v, dtype == SIFT_FP32, vt, counters, stream) != hipSuccess ||
+        launch_prefill(hl, pv, q, k, vt, d_row_ptr, d_col_idx, scale, d_out, d_lse, counters, stream) != hipSuccess)
         return SIFT_ERR_HIP;
     return SIFT_OK;
 }

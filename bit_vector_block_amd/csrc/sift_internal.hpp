@@ -56,9 +56,13 @@ hipError_t launch_decode(const HostLayout &hl, const PlanView &pv, const uint32_
                          const uint32_t *ca, int32_t *row_ptr, int32_t *col_idx, void *workspace,
                          hipStream_t stream);
 hipError_t launch_cast_bf16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);
+// V [N][Hkv][D] (bf16, or fp32 when fp32 is set) -> bf16 V^T [Hkv][D][N] in the prefill layout;
+// also zeroes the 8 row-queue counters the attention kernel claims rows from.
+hipError_t launch_transpose_v(const HostLayout &hl, const void *v, bool fp32, uint16_t *vt, int *counters,
+                              hipStream_t stream);
 hipError_t launch_prefill(const HostLayout &hl, const PlanView &pv, const uint16_t *q,
-                          const uint16_t *k, const uint16_t *v, const int32_t *row_ptr,
-                          const int32_t *col_idx, float scale, float *out, float *lse,
+                          const uint16_t *k, const uint16_t *vt, const int32_t *row_ptr,
+                          const int32_t *col_idx, float scale, float *out, float *lse, int *counters,
                           hipStream_t stream);
 
 }  // namespace sift

@@ -145,8 +145,10 @@ sift_status sift_decode_bits(const sift_layout *layout, const void *d_plan,
  * that, for each row (h, g), visits only the KV tiles listed in the CSR.
  * scores = scale * q.k (scale <= 0 selects 1/sqrt(head_dim)), bf16 MFMA with
  * fp32 accumulation, fp32 softmax, fp32 output d_out [N][Hq][D]; d_lse
- * [Hq][N] may be NULL.  Listed tiles outside [0, G) are skipped.  For
- * SIFT_FP32 inputs the workspace holds their bf16 copies.
+ * [Hq][N] may be NULL.  Listed tiles outside [0, G) are skipped.
+ * d_workspace: >= sift_workspace_bytes(layout, dtype) bytes of scratch; it holds
+ * V transposed to bf16 [Hkv][D][N] (written by the call, in a token order
+ * internal to the library) and, for SIFT_FP32 inputs, the bf16 copies of Q and K.
  * Errors: SIFT_ERR_INVALID, SIFT_ERR_CAPACITY (workspace),
  * SIFT_ERR_UNSUPPORTED (head_dim, tile), SIFT_ERR_HIP.
  */

@@ -100,11 +100,14 @@ def test_prefill_validation_rejects_before_any_launch():
     st = lib.sift_sparse_prefill(lay.ref, vp(1), vp(1), vp(1), vp(1), 7, vp(1), vp(1),
                                  ctypes.c_float(0.0), vp(1), vp(0), vp(0), 0, vp(0))
     assert st == B.SIFT_ERR_INVALID
-    # fp32 inputs need workspace for their bf16 copies
-    st = lib.sift_sparse_prefill(lay.ref, vp(1), vp(1), vp(1), vp(1), B.SIFT_FP32, vp(1), vp(1),
-                                 ctypes.c_float(0.0), vp(1), vp(0), vp(0), 0, vp(0))
-    assert st == B.SIFT_ERR_CAPACITY
-    assert lay.workspace_bytes(B.SIFT_FP32) >= 2 * lay.padded_tokens * (lay.num_q_heads + 2 * lay.num_kv_heads) * lay.head_dim
+    # the workspace holds V^T (bf16), plus the bf16 copies of Q and K for fp32 inputs
+    for dt in (B.SIFT_BF16, B.SIFT_FP32):
+        st = lib.sift_sparse_prefill(lay.ref, vp(1), vp(1), vp(1), vp(1), dt, vp(1), vp(1),
+                                     ctypes.c_float(0.0), vp(1), vp(0), vp(0), 0, vp(0))
+        assert st == B.SIFT_ERR_CAPACITY
+    vt = 2 * lay.padded_tokens * lay.num_kv_heads * lay.head_dim
+    assert lay.workspace_bytes(B.SIFT_BF16) >= vt
+    assert lay.workspace_bytes(B.SIFT_FP32) >= vt + 2 * lay.padded_tokens * (lay.num_q_heads + lay.num_kv_heads) * lay.head_dim
 
 
 @pytest.mark.parametrize("kw,expect", [
