@@ -10,9 +10,12 @@ with every input already resident in HBM.  Prints one JSON line.
 
 value = effective TFLOP/s of the step: computed tiles x 4 * 64 * 64 * D FLOP
 (QK^T and PV, diagonal tiles counted whole, skipped tiles never counted)
-divided by the step time.  The roofline block reports the attention kernel
-alone against the bf16 dense MFMA peak, timed with HIP events on the stream it
-runs on.  The CPU baseline is the fp64 oracle on a bounded sample of rows.
+divided by the step time.  The roofline block reports the sparse_prefill call
+(its V -> V^T transpose, ~3 % of the call, and the attention kernel) against the
+bf16 dense MFMA peak, timed with HIP events on the stream it runs on; the
+full-recompute block runs the same two calls on all-ones bits (dense causal
+attention per request), the pages' speed reference.  The CPU baseline is the
+fp64 oracle on a bounded sample of rows.
 """
 from __future__ import annotations
 
@@ -243,7 +246,7 @@ def main(argv=None):
         "prefill_ms": round(prefill_ms, 5),
         "pct_bf16_peak_step": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
-            "kernel": f"sparse_prefill_kernel<{D}>",
+            "kernel": f"sift_sparse_prefill call: transpose_v_kernel + sparse_prefill_kernel<{D}>",
             "bound": "mfma",
             "achieved": round(achieved, 3),
             "peak": PEAK_BF16_TFLOPS,

@@ -393,29 +393,29 @@ __device__ __forceinline__ void step_compute(WaveState<D> &st, const f32x16 &s_c
 // The row's listed tiles, 64 entries per chunk held across the lanes of one register
 // (lane j of chunk c: entry 64 c + j packed as tile id | (valid tokens - 1) << 25, or -1
 // for a skipped entry), read with v_readlane.  Vector loads keep these reads out of the
-// scalar/LDS counter, so no per-tile scalar-load latency sits on the critical path;
-// chunk c + 1 is fetched 64 tiles ahead of use.
+// scalar/LDS counter, so no per-tile scalar-load latency sits on the critical path.  Chunk
+// c + 1 is fetched as raw tile ids when entry 64 c is reached and packed with its valid
+// counts one step later, so neither load is waited for where it is issued.
 struct TileList {
     int c0, c1;  // chunks c and c + 1
     int c;
+    bool raw1;   // c1 still holds raw ids
 };
 
-// tile ids of entries [base, base + 64) of a row starting at CSR offset e0 with n entries
-__device__ __forceinline__ int fetch_ids(int base, int n, int e0, int G, const int32_t *__restrict__ col_idx,
-                                         int lane) {
+// raw tile ids of entries [base, base + 64) of a row starting at CSR offset e0 with n entries
+// (-1 past the end); no use of the loaded value here, so nothing waits for it
+__device__ __forceinline__ int load_ids(int base, int n, int e0, const int32_t *__restrict__ col_idx, int lane) {
     const int j = base + lane;
-    const int x = j < n ? col_idx[e0 + j] : -1;
-    return (x >= 0 && x < G) ? x : -1;  // out-of-range entries are skipped (masked)
+    return j < n ? col_idx[e0 + j] : -1;
 }
 
-// a tile id packed with its valid-token count (1..64)
-__device__ __forceinline__ int with_valid(int x, const int32_t *__restrict__ tile_valid) {
+// out-of-range entries are skipped (masked)
+__device__ __forceinline__ int valid_id(int x, int G) { return (x >= 0 && x < G) ? x : -1; }
+
+// a raw tile id packed with its valid-token count (1..64)
+__device__ __forceinline__ int with_valid(int x, int G, const int32_t *__restrict__ tile_valid) {
+    x = valid_id(x, G);
     return x >= 0 ? (x | ((tile_valid[x] - 1) << 25)) : -1;
-}
-
-__device__ __forceinline__ int fetch_chunk(int base, int n, int e0, int G, const int32_t *__restrict__ col_idx,
-                                           const int32_t *__restrict__ tile_valid, int lane) {
-    return with_valid(fetch_ids(base, n, e0, G, col_idx, lane), tile_valid);
 }
 
 // Entry i (uniform; c <= i / 64 <= c + 1): tile id (-1: skipped) and valid count (0: skipped).
@@ -428,10 +428,14 @@ __device__ __forceinline__ void list_entry(const TileList &L, int i, int &t, int
 __device__ __forceinline__ void advance_chunk(TileList &L, int i, int n, int e0, int G,
                                               const int32_t *__restrict__ col_idx,
                                               const int32_t *__restrict__ tile_valid, int lane) {
-    if ((i >> 6) != L.c) {  // entry i entered chunk c + 1: shift, fetch chunk c + 2
+    if ((i >> 6) != L.c) {  // entry i entered chunk c + 1: shift, fetch chunk c + 2's ids
         L.c += 1;
         L.c0 = L.c1;
-        L.c1 = fetch_chunk(64 * (L.c + 1), n, e0, G, col_idx, tile_valid, lane);
+        L.c1 = load_ids(64 * (L.c + 1), n, e0, col_idx, lane);
+        L.raw1 = true;
+    } else if (L.raw1) {  // one step later: their valid counts
+        L.c1 = with_valid(L.c1, G, tile_valid);
+        L.raw1 = false;
     }
 }
 
@@ -507,11 +511,46 @@ __device__ inline int resolve_claim(int *__restrict__ counters, const Queues &Q,
     }
 }
 
+// Output merge of the two key halves.  Register i of acc_o[db] holds O^T row (dim)
+// 32 db + 8 (i / 4) + 4 hi + i % 4 of query qi: four consecutive dims per register quad.
+// publish_half: blocks [B HB, B HB + HB) as float4 quads, lane-contiguous in LDS.
+template <int D, int B>
+__device__ __forceinline__ void publish_half(const WaveState<D> &st, f32x4 *dst, int lane) {
+    constexpr int HB = D / 64;
+#pragma unroll
+    for (int j = 0; j < HB; ++j)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const f32x16 &o = st.acc_o[B * HB + j];
+            dst[(j * 4 + a) * 64 + lane] = f32x4{o[4 * a], o[4 * a + 1], o[4 * a + 2], o[4 * a + 3]};
+        }
+}
+
+// finish_half: blocks [B HB, B HB + HB) = own * w0 + partner's * w1, stored to the query's O row
+// (zeros for a padded query), 16 bytes per lane.
+template <int D, int B>
+__device__ __forceinline__ void finish_half(const WaveState<D> &st, const f32x4 *theirs, float *orow, float w0,
+                                            float w1, bool live, int lane, int hi) {
+    constexpr int HB = D / 64;
+#pragma unroll
+    for (int j = 0; j < HB; ++j)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const f32x16 &o = st.acc_o[B * HB + j];
+            const f32x4 t = theirs[(j * 4 + a) * 64 + lane];
+            f32x4 r = {o[4 * a] * w0 + t[0] * w1, o[4 * a + 1] * w0 + t[1] * w1,
+                       o[4 * a + 2] * w0 + t[2] * w1, o[4 * a + 3] * w0 + t[3] * w1};
+            if (!live) r = f32x4{};
+            *reinterpret_cast<f32x4 *>(orow + 32 * (B * HB + j) + 8 * a + 4 * hi) = r;
+        }
+}
+
 // Persistent, two workgroups per CU.  Workgroup b runs on XCD b % 8 and claims rows from that
 // XCD's queue with an atomic counter (zeroed by the V transpose that precedes this kernel),
-// so rows are balanced dynamically, longest first.  The next row is claimed at the start of
-// the current one; its Q, CSR offsets and first list chunk are fetched while the current row
-// finishes (its last tile and the output merge).
+// so rows are balanced dynamically, longest first.  Row r + 1 is claimed when row r starts and
+// known to every wave by row r's first barrier; its CSR offsets load during row r's first
+// tile, its tile ids during the second, its Q during the last, and its first K and V^T tiles
+// stream in while row r's two key halves are merged and stored.
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_prefill_kernel(
     PlanView pv, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -520,12 +559,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float *__restrict__ out, float *__restrict__ lse, int Hq, int Hkv, Queues Qs, int *__restrict__ counters) {
     using C = Cfg<D>;
     constexpr int DB = D / 32;
+    constexpr int HB = DB / 2;  // output blocks each key half finalises
     // four separate tile buffers, so that each LDS read has one known underlying object
     __shared__ __attribute__((aligned(1024))) char kb0[C::KBYTES];
     __shared__ __attribute__((aligned(1024))) char kb1[C::KBYTES];
     __shared__ __attribute__((aligned(1024))) char vb0[C::VBYTES];
     __shared__ __attribute__((aligned(1024))) char vb1[C::VBYTES];
-    __shared__ int s_row;  // the row wave 0 claimed for the workgroup
+    __shared__ int s_row;  // the row the claiming lane resolved for the workgroup
+    static_assert(HB * 16 * 64 * 4 * 2 <= C::VBYTES && HB * 16 * 64 * 4 * 2 + 1024 <= C::KBYTES,
+                  "merge exchange fits kb1 | vb1");
 
     if (!plan_ok(pv)) return;
     const int G = pv.num_tiles;
@@ -535,18 +577,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wavefront
+    __builtin_assume(wave >= 0 && wave < kWaves);
     const int qh = wave & 1, kh = wave >> 1;
     int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
     int qi = 32 * qh + l32;  // this lane's query in the tile
     const bool claimer = tid == 0;
     int cq = home;  // claimer: the queue it draws from
 
-    if (claimer) s_row = resolve_claim(counters, Qs, cq, home, atomicAdd(&counters[home], 1));
+    int pending = 0;  // claimer: a claim kept in flight one row ahead of its use
+    if (claimer) {
+        s_row = resolve_claim(counters, Qs, cq, home, atomicAdd(&counters[home], 1));
+        pending = atomicAdd(&counters[cq % kXcds], 1);
+    }
     lds_barrier();
     int row_idx = s_row;
     if (row_idx < 0) return;
 
-    // the first row's Q, CSR offsets and first list chunk
+    // the first row's Q, CSR offsets and first tile ids
     RowId rid = row_of(row_idx, G, group);
     WaveState<D> st;
     load_q<D>(st, q, rid, Hq, qi, hi);
@@ -556,7 +603,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         e0 = uniform_read(row_ptr, row);
         n = uniform_read(row_ptr, row + 1) - e0;
     }
-    int ids0 = fetch_ids(0, n, e0, G, col_idx, lane);  // tile ids of the row's entries 0..63
+    int ids0 = load_ids(0, n, e0, col_idx, lane);  // raw tile ids of the row's entries 0..63
+    bool first_issued = false;  // K(0) -> kb0 and V(0) -> vb0 already in flight
 
     while (true) {
         lane = (tid & 63) + opaque_zero();
@@ -573,49 +621,60 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         st.m_run = -INFINITY;
         st.l_run = 0.0f;
 
-        // claim the next row now; the claim resolves at this row's last tile
-        int claim = 0;
-        if (claimer) claim = atomicAdd(&counters[cq % kXcds], 1);
-        int nptr = 0;  // lane 0: next row's first CSR offset, lane 1: its end
+        // the next row: its claim went out one row ago and resolves at this row's first barrier,
+        // when the claim for the row after it goes out
         int next_idx = -1;
-        // publish the claimed row (claimer), then every wave starts fetching it
-        auto resolve_next = [&]() {
-            if (claimer) s_row = resolve_claim(counters, Qs, cq, home, claim);
+        int nptr = 0;   // lane 0: next row's first CSR offset, lane 1: its end
+        int nids = -1;  // tile ids of the next row's entries 0..63
+        bool nids_issued = false;
+        auto resolve_next = [&]() {  // every wave; includes a workgroup barrier
+            if (claimer) {
+                const int r = resolve_claim(counters, Qs, cq, home, pending);
+                s_row = r;
+                if (r >= 0) pending = atomicAdd(&counters[cq % kXcds], 1);
+            }
             lds_barrier();
             next_idx = s_row;
-        };
-        auto prefetch_next = [&]() {
             if (next_idx >= 0) {
                 const RowId nid = row_of(next_idx, G, group);
-                load_q<D>(st, q, nid, Hq, qi, hi);
                 nptr = row_ptr[static_cast<int64_t>(nid.h) * G + nid.g + (lane & 1)];
             }
         };
+        auto fetch_next_ids = [&]() {
+            if (next_idx >= 0 && !nids_issued) {
+                const int ne0 = __builtin_amdgcn_readlane(nptr, 0);
+                nids = load_ids(0, __builtin_amdgcn_readlane(nptr, 1) - ne0, ne0, col_idx, lane);
+                nids_issued = true;
+            }
+        };
 
+        int i = 0;
+        f32x16 sa = f32x16{}, sb = f32x16{};
+        float nbias = 0.0f;
         if (n > 0) {
-            // prologue: K(0), V(0), K(1) in flight (their tile ids straight from the id chunk), then
-            // the valid counts of the list; S(0) formed, masked, prepped
-            {
-                const int i0 = __builtin_amdgcn_readlane(ids0, 0), i1 = __builtin_amdgcn_readlane(ids0, 1);
+            // prologue: K(0), V(0) (unless already in flight), K(1); then the list's valid counts;
+            // S(0) formed, masked, prepped
+            if (!first_issued) {
+                const int i0 = valid_id(__builtin_amdgcn_readlane(ids0, 0), G);
                 load_k_tile<D>(k_tile_base<D>(ctx, i0), kb0, wave, off.k);
                 load_vt_tile<D>(vt_tile_base<D>(ctx, i0), vb0, wave, off.v);
-                if (n > 1) load_k_tile<D>(k_tile_base<D>(ctx, i1), kb1, wave, off.k);
             }
+            if (n > 1) load_k_tile<D>(k_tile_base<D>(ctx, valid_id(__builtin_amdgcn_readlane(ids0, 1), G)), kb1, wave, off.k);
             TileList L;
             L.c = 0;
-            L.c0 = with_valid(ids0, pv.tile_valid);
-            L.c1 = n > 64 ? fetch_chunk(64, n, e0, G, col_idx, pv.tile_valid, lane) : -1;
+            L.c0 = with_valid(ids0, G, pv.tile_valid);
+            L.c1 = n > 64 ? load_ids(64, n, e0, col_idx, lane) : -1;
+            L.raw1 = n > 64;
             int t0, v0, t1, v1;
             list_entry(L, 0, t0, v0);
             list_entry(L, 1, t1, v1);  // entry n: t = -1 when past the end
             wait_vmcnt_le(0);
-            __builtin_amdgcn_s_barrier();
-            f32x16 sa = qk_tile<D>(st, kb0, ctx), sb;
+            resolve_next();  // the prologue barrier
+            sa = qk_tile<D>(st, kb0, ctx);
             if (needs_mask(t0, v0, ctx)) apply_mask(sa, t0, v0, ctx);
-            float nbias = lazy_raise<D>(st, tile_max(sa), ctx);
+            nbias = lazy_raise<D>(st, tile_max(sa), ctx);
             // steady state, unrolled by two so that every buffer and score register has a fixed
             // role: step e: wait + barrier; K(e+2) -> free K buffer, V(e+1) -> free V buffer; compute
-            int i = 0;
             int t_a = t1, v_a = v1;  // entry i + 1
             while (i + 1 < n) {
                 advance_chunk(L, i, n, e0, G, col_idx, pv.tile_valid, lane);
@@ -625,6 +684,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 __builtin_amdgcn_s_barrier();  // K(e+1), V(e) landed; everyone left step e-1
                 if (i + 2 < n) load_k_tile<D>(k_tile_base<D>(ctx, t_b), kb0, wave, off.k);
                 load_vt_tile<D>(vt_tile_base<D>(ctx, t_a), vb1, wave, off.v);
+                if (i == 0) fetch_next_ids();  // the next row's offsets landed with the wait above
                 __builtin_amdgcn_sched_barrier(0);
                 step_compute<D>(st, sa, sb, nbias, kb1, vb0, t_a, v_a, ctx);
                 ++i;
@@ -644,100 +704,75 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 v_a = v_b;
             }
             // last listed tile: softmax + PV only (its scores in sa for even i, its V^T in vb[i % 2]);
-            // Q is no longer needed, so the next row's Q and CSR offsets start loading now
+            // Q is no longer needed, so the next row's Q starts loading now
             wait_vmcnt_le(0);
-            resolve_next();
-            prefetch_next();
-            if ((i & 1) == 0) exp_pv_tile<D>(st, sa, nbias, vb0, ctx);
-            else exp_pv_tile<D>(st, sb, nbias, vb1, ctx);
+            __builtin_amdgcn_s_barrier();
         } else {
             resolve_next();
-            prefetch_next();
+        }
+        fetch_next_ids();
+        if (next_idx >= 0) load_q<D>(st, q, row_of(next_idx, G, group), Hq, qi, hi);
+        if (n > 0) {
+            if ((i & 1) == 0) exp_pv_tile<D>(st, sa, nbias, vb0, ctx);
+            else exp_pv_tile<D>(st, sb, nbias, vb1, ctx);
         }
 
-        // merge the two key halves: waves with kh = 1 publish, waves with kh = 0 combine
+        // merge the two key halves: wave (qh, kh) finalises output blocks [kh HB, kh HB + HB) and
+        // publishes the other HB blocks, and its (m, l), for its partner (qh, 1 - kh)
         const float l_tot = pair_sum(st.l_run);
-        float *X = reinterpret_cast<float *>(kb0);  // [D/2 registers][2 query halves][64 lanes] (kb0 + kb1)
-        float *ML = reinterpret_cast<float *>(vb0);  // [2 query halves][32 queries][m, l]
-        lds_barrier();
-        if (kh == 1) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = db * 16 + i;  // first D/4 registers in kb0, the rest in kb1
-                    float *dst = r < D / 4 ? X : reinterpret_cast<float *>(kb1);
-                    dst[(((r % (D / 4)) * 2) + qh) * 64 + lane] = st.acc_o[db][i];
-                }
+        char *xq = qh ? vb1 : kb1;  // [2 publishers kh][HB blocks][4 quads][64 lanes] float4
+        float *ML = reinterpret_cast<float *>(kb1 + 2 * HB * 16 * 64 * 4);  // [qh][kh][32 queries][m, l]
+        lds_barrier();  // every wave is done with the last tile's buffers
+        {
+            f32x4 *mine = reinterpret_cast<f32x4 *>(xq) + kh * HB * 4 * 64;
+            // register arrays take compile-time indices only: one branch per key half
+            if (kh == 0) publish_half<D, 1>(st, mine, lane);
+            else publish_half<D, 0>(st, mine, lane);
             if (hi == 0) {
-                ML[(qh * 32 + l32) * 2 + 0] = st.m_run;
-                ML[(qh * 32 + l32) * 2 + 1] = l_tot;
+                ML[((qh * 2 + kh) * 32 + l32) * 2 + 0] = st.m_run;
+                ML[((qh * 2 + kh) * 32 + l32) * 2 + 1] = l_tot;
             }
         }
-        lds_barrier();
-        float m_fin = -INFINITY, l_fin = 0.0f;
-        if (kh == 0) {
-            const float m1 = ML[(qh * 32 + l32) * 2 + 0];
-            const float l1 = ML[(qh * 32 + l32) * 2 + 1];
-            m_fin = fmaxf(st.m_run, m1);
-            const float a0 = (st.m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((st.m_run - m_fin) * scale_log2);
-            const float a1 = (m1 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m1 - m_fin) * scale_log2);
-            l_fin = l_tot * a0 + l1 * a1;
-            const float inv = l_fin > 0.0f ? 1.0f / l_fin : 0.0f;
-            const float w0 = a0 * inv, w1 = a1 * inv;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = db * 16 + i;
-                    const float *src = r < D / 4 ? X : reinterpret_cast<const float *>(kb1);
-                    st.acc_o[db][i] = st.acc_o[db][i] * w0 + src[(((r % (D / 4)) * 2) + qh) * 64 + lane] * w1;
-                }
-        }
-        // the next row's first list chunk: its tile ids now, their valid counts after the stores
+        // the next row's first K and V^T tiles stream in during the merge
         const bool has_next = next_idx >= 0;
-        int e0n = 0, nn = 0, ids = -1;
+        int e0n = 0, nn = 0;
         if (has_next) {
             e0n = __builtin_amdgcn_readlane(nptr, 0);
             nn = __builtin_amdgcn_readlane(nptr, 1) - e0n;
-            ids = fetch_ids(0, nn, e0n, G, col_idx, lane);
-        }
-        lds_barrier();
-        // output tile staged in kb0|kb1 as [64 rows][D/4 float4 chunks], chunk c of row r at
-        // c ^ (r % 32); rows 0..31 in kb0, rows 32..63 in kb1
-        constexpr int C4 = D / 4;
-        auto orow = [&](int r) -> float * {
-            return reinterpret_cast<float *>(r < 32 ? kb0 : kb1) + (r & 31) * D;
-        };
-        if (kh == 0) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const f32x4 o4 = {st.acc_o[db][4 * i4 + 0], st.acc_o[db][4 * i4 + 1],
-                                      st.acc_o[db][4 * i4 + 2], st.acc_o[db][4 * i4 + 3]};
-                    const int c4 = 8 * db + 2 * i4 + hi;
-                    *reinterpret_cast<f32x4 *>(orow(qi) + 4 * (c4 ^ (qi & (C4 - 1)))) = o4;
-                }
-            if (lse != nullptr && hi == 0) {
-                const bool live = qi < q_valid && l_fin > 0.0f;
-                lse[static_cast<int64_t>(h) * N + tok0 + qi] = live ? m_fin * scale + logf(l_fin) : -INFINITY;
+            if (nn > 0) {
+                const RowId nid = row_of(next_idx, G, group);
+                const int i0 = valid_id(__builtin_amdgcn_readlane(nids, 0), G);
+                const RowCtx nctx{k, vt, N, Hkv, nid.kvh, nid.g, qi, wave, lane, scale_log2, lazy_raw};
+                load_k_tile<D>(k_tile_base<D>(nctx, i0), kb0, wave, off.k);
+                load_vt_tile<D>(vt_tile_base<D>(nctx, i0), vb0, wave, off.v);
             }
         }
         lds_barrier();
-        for (int x = tid; x < 64 * C4; x += kThreads) {
-            const int r = x / C4, c4 = x % C4;
-            f32x4 val = *reinterpret_cast<const f32x4 *>(orow(r) + 4 * (c4 ^ (r & (C4 - 1))));
-            if (r >= q_valid) val = f32x4{};
-            // written once: non-temporal, so 32 KB of output per row does not evict K/V tiles
-            __builtin_nontemporal_store(val, reinterpret_cast<f32x4 *>(out + ((tok0 + r) * Hq + h) * D + 4 * c4));
+        {
+            const f32x4 *theirs = reinterpret_cast<const f32x4 *>(xq) + (1 - kh) * HB * 4 * 64;
+            const float m1 = ML[((qh * 2 + (1 - kh)) * 32 + l32) * 2 + 0];
+            const float l1 = ML[((qh * 2 + (1 - kh)) * 32 + l32) * 2 + 1];
+            const float m_fin = fmaxf(st.m_run, m1);
+            const float a0 = (st.m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((st.m_run - m_fin) * scale_log2);
+            const float a1 = (m1 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m1 - m_fin) * scale_log2);
+            const float l_fin = l_tot * a0 + l1 * a1;
+            const float inv = l_fin > 0.0f ? 1.0f / l_fin : 0.0f;
+            const float w0 = a0 * inv, w1 = a1 * inv;
+            const bool live = qi < q_valid;
+            float *orow = out + ((tok0 + qi) * Hq + h) * D;
+            if (kh == 0) finish_half<D, 0>(st, theirs, orow, w0, w1, live, lane, hi);
+            else finish_half<D, 1>(st, theirs, orow, w0, w1, live, lane, hi);
+            if (lse != nullptr && kh == 0 && hi == 0)
+                lse[static_cast<int64_t>(h) * N + tok0 + qi] =
+                    (live && l_fin > 0.0f) ? m_fin * scale + logf(l_fin) : -INFINITY;
         }
         if (!has_next) break;
-        ids0 = ids;
-        lds_barrier();  // every wave has read the staged output before the next row's tiles land
+        lds_barrier();  // every wave has read the exchange before the next row's K(1) lands in kb1
         rid = row_of(next_idx, G, group);
         e0 = e0n;
         n = nn;
+        ids0 = nids;
+        first_issued = nn > 0;
     }
 }
 

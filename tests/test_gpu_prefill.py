@@ -44,6 +44,35 @@ def test_prefill_random_small(seed):
     _full_check(case)
 
 
+# KV-head counts that exercise each way rows are split over the 8 XCD work queues: Hkv dividing 8
+# (heads shared by 8 / Hkv queues, interleaved), 8 dividing Hkv (heads dealt to queues in turn)
+# and neither (contiguous eighths of the row order); the small cases also leave queues empty,
+# so workgroups drain other queues.
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (16, 16, 64), (6, 3, 128), (12, 6, 64), (5, 5, 128)])
+def test_prefill_queue_modes(hq, hkv, d):
+    case = W.random_small_case(100 + hq + hkv, max_requests=2, max_docs=3, max_tiles=6, hq=hq, hkv=hkv, d=d)
+    _full_check(case)
+
+
+def test_prefill_many_rows_per_workgroup():
+    """More rows than the 512 persistent workgroups hold at once (every workgroup takes several
+    rows, prefetching the next row's tiles during the current row's merge), with 64-entry list
+    chunks crossed (rows longer than 64 tiles)."""
+    case = W.make_case("many-rows", 1200, [6], [64 * 30] * 6, [200], 8, 2, 64,
+                       np.full((1, 8), 0.6), np.full((1, 8), 0.5))
+    out, lse = gpu_prefill(case)
+    valid = valid_tokens(case)
+    rng = np.random.default_rng(5)
+    heads, toks = _sample_pairs(case, rng, 800)
+    ref, ref_lse = oracle.attention(case, heads=heads, tokens=toks)
+    keep = valid[toks]
+    assert_close(out[toks, heads][keep], ref[keep], "many rows")
+    fin = np.isfinite(ref_lse)
+    assert np.max(np.abs(lse[heads, toks][fin] - ref_lse[fin]), initial=0.0) <= LSE_ABS
+    rp, _ = oracle.decode(case)
+    assert (np.diff(rp) > 64).any(), "some row must span more than one 64-entry list chunk"
+
+
 @pytest.mark.parametrize("seed", range(3))
 def test_prefill_all_ones_is_dense_causal(seed):
     case = W.random_small_case(50 + seed, hq=4, hkv=2, d=128, max_tiles=6)
