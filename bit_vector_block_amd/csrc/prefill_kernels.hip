@@ -171,13 +171,9 @@ __device__ inline float pair_sum(float x) {  // sum over lanes l and l ^ 32
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// max of three without the NaN-quieting canonicalisations fmaxf brings; inputs are MFMA
-// results or -inf from masking, and a NaN score can only come from masked padded keys
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-    float r;
-    asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
+// max of three (v_max3_f32).  Plain code, not inline asm: the inputs are MFMA results, and
+// only the compiler's hazard tracking inserts the wait states a VALU read of an MFMA result needs.
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // Online-softmax state of one wavefront (32 queries x one 32-key half of each tile).
 template <int D>
@@ -785,13 +781,30 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const T *__restrict__ 
     // the attention kernel that follows on the stream claims rows from these counters
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kXcds) counters[threadIdx.x] = 0;
     constexpr int LD = D + 2;  // padded LDS row (bf16 elements): column reads hit distinct banks
+    constexpr int CH = D / 8;  // 8-element chunks per token row
     __shared__ uint16_t tile[64 * LD];
     const int t = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
     const int64_t tok0 = static_cast<int64_t>(t) * kTile;
-    for (int x = tid; x < 64 * D; x += 256) {
-        const int r = x / D, d = x % D;
-        const T val = v[((tok0 + r) * Hkv + kvh) * D + d];
-        tile[r * LD + d] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));
+    // read: 8 consecutive elements (16 or 32 bytes) of one token row per thread and pass
+    for (int x = tid; x < 64 * CH; x += 256) {
+        const int r = x / CH, c = x % CH;
+        const T *src = v + ((tok0 + r) * Hkv + kvh) * D + 8 * c;
+        uint16_t *dst = tile + r * LD + 8 * c;
+        if constexpr (sizeof(T) == 2) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(src);
+            const uint32_t p[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                dst[2 * j] = static_cast<uint16_t>(p[j] & 0xFFFFu);
+                dst[2 * j + 1] = static_cast<uint16_t>(p[j] >> 16);
+            }
+        } else {
+            const float4 a = *reinterpret_cast<const float4 *>(src);
+            const float4 b = *reinterpret_cast<const float4 *>(src + 4);
+            const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dst[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(f[j]));
+        }
     }
     __syncthreads();
     // V^T row d of this tile: 64 stored positions; thread writes 8 consecutive positions

@@ -301,6 +301,11 @@ sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan, c
     if (hl.G == 0) return SIFT_OK;
     if (!d_plan || !d_q || !d_k || !d_v || !d_row_ptr || !d_col_idx || !d_out)
         return SIFT_ERR_INVALID;
+    // Q/K/V are read and O written in 16-byte vectors
+    auto aligned16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if (!aligned16(d_q) || !aligned16(d_k) || !aligned16(d_v) || !aligned16(d_out) ||
+        (d_workspace && !aligned16(d_workspace)))
+        return SIFT_ERR_INVALID;
     if (!(scale > 0.0f)) scale = 1.0f / sqrtf(float(hl.D));
     if (!isfinite(scale)) return SIFT_ERR_INVALID;
     const size_t need = prefill_workspace_bytes(hl, dtype);

@@ -284,6 +284,20 @@ def random_small_case(seed, max_requests=2, max_docs=3, max_tiles=4, hq=2, hkv=1
                      hq, hkv, d, la, ca, dtype, rng=rng)
 
 
+def layer_bits(case: Case, layer: int, la_p, ca_p):
+    """LA/CA bits of another layer on the same layout: the same draw as make_case (Bernoulli per
+    (request, q head) density, diagonal and page 0 forced) from the stream seeded by
+    (case seed, layer).  la_p / ca_p: scalars or arrays [R, Hq].  Returns (la_bool, ca_bool)."""
+    rng = np.random.default_rng([int(case.seed), 7919, int(layer)])
+    R, hq = len(case.req_num_docs), case.num_q_heads
+    la_p = np.broadcast_to(np.asarray(la_p, dtype=np.float64), (R, hq))
+    ca_p = np.broadcast_to(np.asarray(ca_p, dtype=np.float64), (R, hq))
+    doc_req = np.repeat(np.arange(R), case.req_num_docs)
+    la = [_draw_la(rng, tiles_of(int(n_d)), hq, la_p[doc_req[i]]) for i, n_d in enumerate(case.doc_len)]
+    ca = [_draw_ca(rng, tiles_of(int(n_d)), hq, ca_p[doc_req[i]]) for i, n_d in enumerate(case.doc_len)]
+    return la, ca
+
+
 def with_bits(case: Case, la_bool, ca_bool) -> Case:
     """Same layout and values, other bits (used to build the special cases)."""
     la_words, ca_words = pack_bits(la_bool, ca_bool)

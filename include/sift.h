@@ -146,6 +146,7 @@ sift_status sift_decode_bits(const sift_layout *layout, const void *d_plan,
  * scores = scale * q.k (scale <= 0 selects 1/sqrt(head_dim)), bf16 MFMA with
  * fp32 accumulation, fp32 softmax, fp32 output d_out [N][Hq][D]; d_lse
  * [Hq][N] may be NULL.  Listed tiles outside [0, G) are skipped.
+ * d_q, d_k, d_v, d_out and d_workspace must be 16-byte aligned (SIFT_ERR_INVALID otherwise).
  * d_workspace: >= sift_workspace_bytes(layout, dtype) bytes of scratch; it holds
  * V transposed to bf16 [Hkv][D][N] (written by the call, in a token order
  * internal to the library) and, for SIFT_FP32 inputs, the bf16 copies of Q and K.

@@ -100,10 +100,15 @@ def test_prefill_validation_rejects_before_any_launch():
     st = lib.sift_sparse_prefill(lay.ref, vp(1), vp(1), vp(1), vp(1), 7, vp(1), vp(1),
                                  ctypes.c_float(0.0), vp(1), vp(0), vp(0), 0, vp(0))
     assert st == B.SIFT_ERR_INVALID
+    # Q/K/V/O must be 16-byte aligned (fake, never dereferenced, addresses)
+    a = vp(4096)
+    st = lib.sift_sparse_prefill(lay.ref, a, vp(4096 + 8), a, a, B.SIFT_BF16, a, a,
+                                 ctypes.c_float(0.0), a, vp(0), a, 1 << 30, vp(0))
+    assert st == B.SIFT_ERR_INVALID
     # the workspace holds V^T (bf16), plus the bf16 copies of Q and K for fp32 inputs
     for dt in (B.SIFT_BF16, B.SIFT_FP32):
-        st = lib.sift_sparse_prefill(lay.ref, vp(1), vp(1), vp(1), vp(1), dt, vp(1), vp(1),
-                                     ctypes.c_float(0.0), vp(1), vp(0), vp(0), 0, vp(0))
+        st = lib.sift_sparse_prefill(lay.ref, a, a, a, a, dt, a, a,
+                                     ctypes.c_float(0.0), a, vp(0), vp(0), 0, vp(0))
         assert st == B.SIFT_ERR_CAPACITY
     vt = 2 * lay.padded_tokens * lay.num_kv_heads * lay.head_dim
     assert lay.workspace_bytes(B.SIFT_BF16) >= vt

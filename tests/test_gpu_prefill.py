@@ -54,6 +54,19 @@ def test_prefill_queue_modes(hq, hkv, d):
     _full_check(case)
 
 
+@pytest.mark.parametrize("seed,layer", [(300, 2), (301, 1), (301, 3)])
+def test_prefill_repeat_calls_are_bit_identical(seed, layer):
+    """Which workgroup takes a row varies from call to call; the result must not.  (These cases
+    once differed between calls in a few queries of a diagonal, partial tile: the max of the
+    scores was read from the MFMA result registers too early.)"""
+    base = W.random_small_case(seed, max_requests=2, max_docs=3, max_tiles=5, hq=4, hkv=2, d=128)
+    case = W.with_bits(base, *W.layer_bits(base, layer, 0.4, 0.3))
+    first, first_lse = gpu_prefill(case)
+    for _ in range(7):
+        again, again_lse = gpu_prefill(case)
+        assert np.array_equal(again, first) and np.array_equal(again_lse, first_lse)
+
+
 def test_prefill_many_rows_per_workgroup():
     """More rows than the 512 persistent workgroups hold at once (every workgroup takes several
     rows, prefetching the next row's tiles during the current row's merge), with 64-entry list
