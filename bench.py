@@ -132,6 +132,8 @@ def main(argv=None):
                     help="CPU work budget of the oracle baseline (0 disables it)")
     ap.add_argument("--layers", type=int, default=32,
                     help="layers of the pipelined multi-layer run (per-layer bits from pinned host memory; 0: skip)")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the fused decode-in-attention timing (sift_sparse_prefill_bits)")
     ap.add_argument("--no-full-recompute", action="store_true",
                     help="skip the full-recompute comparison (same kernels on all-ones bits)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -274,6 +276,25 @@ def main(argv=None):
             "computed_tiles": nnz1,
             "tflops": round(float(nnz1) * 4.0 * 64 * 64 * D / (pre1 * 1e-3) / 1e12, 3),
             "speedup_of_sparse_layer": round(ms1 / ms_per_step, 3),
+        }
+    if not args.no_fused:
+        # the same layer with the decode fused into the attention (sift_sparse_prefill_bits: a
+        # per-head pre-pass of CA page lists, then lists built from the bits inside the kernel)
+        log("fused decode-in-attention")
+        for _ in range(max(args.warmup, 1)):
+            sift.sparse_prefill_bits(lay, la, ca, q, k, v, plan=plan, workspace=ws, out=out)
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for _ in range(args.steps):
+            sift.sparse_prefill_bits(lay, la, ca, q, k, v, plan=plan, workspace=ws, out=out)
+        f1.record(stream)
+        torch.cuda.synchronize()
+        ms_f = f0.elapsed_time(f1) / args.steps
+        result["fused_decode"] = {
+            "ms_per_layer": round(ms_f, 5),
+            "tflops": round(flops / (ms_f * 1e-3) / 1e12, 3),
+            "vs_decode_plus_prefill": round(ms_f / ms_per_step, 3),
         }
     if args.layers > 0:
         # a stack of layers: every layer's LA/CA bits differ (drawn at the workload's densities) and

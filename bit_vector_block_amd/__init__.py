@@ -3,12 +3,13 @@
 Two hand-written HIP kernels behind the C ABI of include/sift.h:
   * ``decode_bits``    -- LA/CA bit vectors -> per-(head, query tile) CSR of KV tiles;
   * ``sparse_prefill`` -- block-sparse causal GQA attention over that CSR
-                          (bf16 MFMA, online softmax, fp32 output).
-This package is the ctypes binding (argument marshalling) plus the seeded
-synthetic workloads in ``workloads``.
+                          (bf16 MFMA, online softmax, fp32 output);
+  * ``sparse_prefill_bits`` -- the same attention with the decode fused in (reads the bits).
+This package is the ctypes binding (argument marshalling), the seeded synthetic
+workloads in ``workloads`` and the multi-layer stream orchestration in ``pipeline``.
 """
 from ._binding import (SIFT_BF16, SIFT_FP32, Layout, SiftError, decode_bits, default_scale,
-                       library, plan_upload, sparse_prefill)
+                       library, plan_upload, sparse_prefill, sparse_prefill_bits)
 
-__all__ = ["Layout", "SiftError", "decode_bits", "sparse_prefill", "plan_upload", "library",
-           "default_scale", "SIFT_BF16", "SIFT_FP32"]
+__all__ = ["Layout", "SiftError", "decode_bits", "sparse_prefill", "sparse_prefill_bits", "plan_upload",
+           "library", "default_scale", "SIFT_BF16", "SIFT_FP32"]

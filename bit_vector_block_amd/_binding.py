@@ -22,7 +22,8 @@ SIFT_BF16, SIFT_FP32 = 0, 1
 EXPORTED = (
     "sift_num_tiles", "sift_padded_tokens", "sift_num_rows", "sift_la_words", "sift_ca_words",
     "sift_csr_max_nnz", "sift_plan_bytes", "sift_workspace_bytes", "sift_plan_upload",
-    "sift_decode_bits", "sift_sparse_prefill", "sift_status_string", "sift_abi_version",
+    "sift_decode_bits", "sift_sparse_prefill", "sift_sparse_prefill_bits", "sift_status_string",
+    "sift_abi_version",
 )
 
 
@@ -72,6 +73,9 @@ def _lib():
     lib.sift_sparse_prefill.argtypes = [L, vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_float,
                                         vp, vp, vp, sz, vp]
     lib.sift_sparse_prefill.restype = ctypes.c_int
+    lib.sift_sparse_prefill_bits.argtypes = [L, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_float,
+                                             vp, vp, vp, sz, vp]
+    lib.sift_sparse_prefill_bits.restype = ctypes.c_int
     lib.sift_status_string.argtypes = [ctypes.c_int]
     lib.sift_status_string.restype = ctypes.c_char_p
     lib.sift_abi_version.argtypes = []
@@ -224,6 +228,42 @@ def sparse_prefill(layout: Layout, q, k, v, row_ptr, col_idx, plan=None, scale: 
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
         ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream_handle(torch, device)),
         "sift_sparse_prefill")
+    return out, (lse if want_lse else None)
+
+
+def sparse_prefill_bits(layout: Layout, la, ca, q, k, v, plan=None, scale: Optional[float] = None,
+                        want_lse: bool = False, workspace=None, out=None, lse=None):
+    """The same attention with the decode fused in (no CSR): la / ca are the layer's bit words
+    (int32 tensors on the device, as for decode_bits).  Returns (out, lse or None)."""
+    import torch
+    device = q.device
+    n, hq, hkv, d = layout.padded_tokens, layout.num_q_heads, layout.num_kv_heads, layout.head_dim
+    if q.dtype == torch.bfloat16:
+        dt = SIFT_BF16
+    elif q.dtype == torch.float32:
+        dt = SIFT_FP32
+    else:
+        raise ValueError("q/k/v must be bfloat16 or float32")
+    for name, t, shape in (("q", q, (n, hq, d)), ("k", k, (n, hkv, d)), ("v", v, (n, hkv, d))):
+        if tuple(t.shape) != shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != device:
+            raise ValueError(f"{name}: need a contiguous {q.dtype} tensor of shape {shape} on {device}")
+    for name, t, words in (("la", la, layout.la_words), ("ca", ca, layout.ca_words)):
+        if t.dtype != torch.int32 or t.device != device or t.numel() < max(words, 1):
+            raise ValueError(f"{name}: need an int32 tensor of >= {words} words on {device}")
+    if plan is None:
+        plan = plan_upload(layout, device)
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.float32, device=device)
+    if want_lse and lse is None:
+        lse = torch.empty((hq, n), dtype=torch.float32, device=device)
+    ws, ws_bytes = _workspace(torch, layout, dt, device, workspace)
+    sc = 0.0 if scale is None else float(scale)
+    _check(_lib().sift_sparse_prefill_bits(
+        layout.ref, ctypes.c_void_p(plan.data_ptr()), ctypes.c_void_p(la.data_ptr()),
+        ctypes.c_void_p(ca.data_ptr()), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+        ctypes.c_void_p(v.data_ptr()), dt, ctypes.c_float(sc), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), ctypes.c_void_p(ws.data_ptr()), ws_bytes,
+        _stream_handle(torch, device)), "sift_sparse_prefill_bits")
     return out, (lse if want_lse else None)
 
 

@@ -179,7 +179,87 @@ __global__ __launch_bounds__(64 * kFillWaves) void decode_fill_kernel(
     }
 }
 
+// Pre-pass of the fused path (no CSR): one workgroup per q head h.
+//   ca_prefix[h][d] : CA entries of the earlier documents of d's request (request-local);
+//   ca_list[h][req_first[b] + k] : the k-th CA-marked page of request b, in document order --
+//                      the CA part of every document row of the request is a leading slice of it;
+//   rowinfo[h][g]   : what the attention kernel needs to build row (h, g)'s list itself:
+//                      {n, ca_n (-1: question row, dense range), ca_base, la_word, la_lo, t0, r, 0}.
+__global__ __launch_bounds__(kCountThreads) void bits_prepass_kernel(
+    PlanView pv, const uint32_t *__restrict__ la, const uint32_t *__restrict__ ca,
+    int32_t *__restrict__ ca_prefix, int32_t *__restrict__ ca_list, int32_t *__restrict__ rowinfo) {
+    if (!plan_ok(pv)) return;
+    const int h = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ndocs = pv.num_docs, G = pv.num_tiles;
+    int32_t *pref = ca_prefix + static_cast<int64_t>(h) * ndocs;
+    for (int d = tid; d < ndocs; d += kCountThreads) {
+        const uint32_t *vec = ca + pv.doc_ca_off[d] + h * pv.doc_ca_w[d];
+        pref[d] = popcount_range(vec, 0, pv.doc_tiles[d] - 1);
+    }
+    __syncthreads();
+    for (int b = tid; b < pv.num_requests; b += kCountThreads) {
+        int acc = 0;
+        const int d0 = pv.req_first_doc[b], d1 = d0 + pv.req_ndocs[b];
+        for (int d = d0; d < d1; ++d) {
+            const int c = pref[d];
+            pref[d] = acc;
+            acc += c;
+        }
+    }
+    __syncthreads();
+    // CA pages of each document, one wavefront per document: ballot and lane rank place them
+    int32_t *lst = ca_list + static_cast<int64_t>(h) * G;
+    for (int d = wave; d < ndocs; d += kCountThreads / 64) {
+        const uint32_t *vec = ca + pv.doc_ca_off[d] + h * pv.doc_ca_w[d];
+        const int T = pv.doc_tiles[d], t0 = pv.doc_first[d];
+        int pos = pv.req_first[pv.doc_req[d]] + pref[d];
+        for (int c0 = 0; c0 < T; c0 += 64) {
+            const int c = c0 + lane;
+            const bool bit = c < T && ((vec[c >> 5] >> (c & 31)) & 1u);
+            const uint64_t mask = __ballot(bit);
+            if (bit) lst[pos + lane_rank(mask)] = t0 + c;
+            pos += __popcll(mask);
+        }
+    }
+    // per-row records
+    for (int g = tid; g < G; g += kCountThreads) {
+        int32_t *ri = rowinfo + (static_cast<int64_t>(h) * G + g) * 8;
+        const int d = pv.tile_doc[g];
+        if (d < 0) {
+            const int first = pv.req_first[-d - 1];
+            ri[0] = g - first + 1;
+            ri[1] = -1;
+            ri[2] = 0;
+            ri[3] = 0;
+            ri[4] = 0;
+            ri[5] = first;
+            ri[6] = 0;
+        } else {
+            const int r = pv.tile_local[g];
+            const int lo = r * (r + 1) / 2;
+            const int la_word = pv.doc_la_off[d] + h * pv.doc_la_w[d];
+            const int la_n = popcount_range(la + la_word, lo, lo + r);
+            ri[0] = pref[d] + la_n;
+            ri[1] = pref[d];
+            ri[2] = h * G + pv.req_first[pv.doc_req[d]];
+            ri[3] = la_word;
+            ri[4] = lo;
+            ri[5] = pv.doc_first[d];
+            ri[6] = r;
+        }
+        ri[7] = 0;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_bits_prepass(const HostLayout &hl, const PlanView &pv, const uint32_t *la, const uint32_t *ca,
+                               int32_t *ca_prefix, int32_t *ca_list, int32_t *rowinfo, hipStream_t stream) {
+    if (hl.G == 0) return hipSuccess;
+    bits_prepass_kernel<<<hl.Hq, kCountThreads, 0, stream>>>(pv, la, ca, ca_prefix, ca_list, rowinfo);
+    return hipGetLastError();
+}
 
 hipError_t launch_decode(const HostLayout &hl, const PlanView &pv, const uint32_t *la,
                          const uint32_t *ca, int32_t *row_ptr, int32_t *col_idx, void *workspace,

@@ -61,6 +61,7 @@ sift_status build_layout(const sift_layout *layout, HostLayout *out) {
             int64_t tb = 0;
             for (int32_t i = 0; i < L.req_num_docs[b]; ++i, ++d) {
                 const int64_t T = ceil_div(L.doc_len[d], kTile);
+                if (T > hl.max_doc_tiles) hl.max_doc_tiles = T;
                 tb += T;
                 la_words += static_cast<int64_t>(L.num_q_heads) * ceil_div(T * (T + 1) / 2, 32);
                 ca_words += static_cast<int64_t>(L.num_q_heads) * ceil_div(T, 32);
@@ -186,13 +187,19 @@ size_t decode_workspace_bytes(const HostLayout &hl) {
 }
 
 // Prefill scratch: 256 bytes of row-queue counters, V^T (bf16 [Hkv][D][N]); for SIFT_FP32
-// inputs the bf16 copies of Q and K follow.
+// inputs the bf16 copies of Q and K follow.  The fused path (no CSR) appends its pre-pass
+// tables: ca_prefix [Hq][ndocs], ca_list [Hq][G], rowinfo [Hq][G][8] (int32).
 constexpr size_t kCounterBytes = 256;
 static size_t prefill_workspace_bytes(const HostLayout &hl, sift_dtype dtype) {
     const size_t N = size_t(hl.G) * kTile;
     const size_t vt = kCounterBytes + align256(2 * N * hl.Hkv * hl.D);
     if (dtype != SIFT_FP32) return vt;
     return vt + align256(2 * N * hl.Hq * hl.D) + align256(2 * N * hl.Hkv * hl.D);
+}
+static size_t bits_tables_bytes(const HostLayout &hl) {
+    const size_t rows = size_t(hl.Hq) * size_t(hl.G > 0 ? hl.G : 1);
+    return align256(4 * size_t(hl.Hq) * size_t(hl.ndocs > 0 ? hl.ndocs : 1)) + align256(4 * rows) +
+           align256(32 * rows);
 }
 
 }  // namespace sift
@@ -253,7 +260,7 @@ size_t sift_workspace_bytes(const sift_layout *layout, sift_dtype dtype) {
     HostLayout hl;
     if (build_layout(layout, &hl) != SIFT_OK) return 0;
     if (dtype != SIFT_BF16 && dtype != SIFT_FP32) return 0;
-    return std::max(decode_workspace_bytes(hl), prefill_workspace_bytes(hl, dtype));
+    return std::max(decode_workspace_bytes(hl), prefill_workspace_bytes(hl, dtype) + bits_tables_bytes(hl));
 }
 
 sift_status sift_plan_upload(const sift_layout *layout, void *d_plan, size_t plan_bytes,
@@ -329,7 +336,61 @@ sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan, c
         k = kb;
     }
     if (launch_transpose_v(hl, d_v, dtype == SIFT_FP32, vt, counters, stream) != hipSuccess ||
-        launch_prefill(hl, pv, q, k, vt, d_row_ptr, d_col_idx, scale, d_out, d_lse, counters, stream) != hipSuccess)
+        launch_prefill(hl, pv, q, k, vt, d_row_ptr, d_col_idx, nullptr, nullptr, nullptr, scale, d_out, d_lse,
+                       counters, stream) != hipSuccess)
+        return SIFT_ERR_HIP;
+    return SIFT_OK;
+}
+
+sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_plan, const uint32_t *d_la,
+                                     const uint32_t *d_ca, const void *d_q, const void *d_k, const void *d_v,
+                                     sift_dtype dtype, float scale, float *d_out, float *d_lse,
+                                     void *d_workspace, size_t workspace_bytes, hipStream_t stream) {
+    HostLayout hl;
+    sift_status st = build_layout(layout, &hl);
+    if (st != SIFT_OK) return st;
+    if (dtype != SIFT_BF16 && dtype != SIFT_FP32) return SIFT_ERR_INVALID;
+    if (hl.G == 0) return SIFT_OK;
+    if (!d_plan || !d_q || !d_k || !d_v || !d_out) return SIFT_ERR_INVALID;
+    if ((hl.la_words > 0 && !d_la) || (hl.ca_words > 0 && !d_ca)) return SIFT_ERR_INVALID;
+    auto aligned16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if (!aligned16(d_q) || !aligned16(d_k) || !aligned16(d_v) || !aligned16(d_out) ||
+        (d_workspace && !aligned16(d_workspace)))
+        return SIFT_ERR_INVALID;
+    // a row's LA bits are read as at most 64 words: documents of at most 1984 tiles
+    if (hl.max_doc_tiles > 1984) return SIFT_ERR_UNSUPPORTED;
+    if (!(scale > 0.0f)) scale = 1.0f / sqrtf(float(hl.D));
+    if (!isfinite(scale)) return SIFT_ERR_INVALID;
+    const size_t base = prefill_workspace_bytes(hl, dtype);
+    const size_t need = base + bits_tables_bytes(hl);
+    if (!d_workspace || workspace_bytes < need) return SIFT_ERR_CAPACITY;
+    const PlanView pv = plan_view(hl, d_plan);
+    const uint16_t *q = static_cast<const uint16_t *>(d_q);
+    const uint16_t *k = static_cast<const uint16_t *>(d_k);
+    const int64_t N = int64_t(hl.G) * kTile;
+    const int64_t nq = N * hl.Hq * hl.D, nkv = N * hl.Hkv * hl.D;
+    char *ws = static_cast<char *>(d_workspace);
+    int *counters = reinterpret_cast<int *>(ws);
+    uint16_t *vt = reinterpret_cast<uint16_t *>(ws + kCounterBytes);
+    if (dtype == SIFT_FP32) {
+        char *ws2 = ws + kCounterBytes + align256(2 * size_t(nkv));
+        uint16_t *qb = reinterpret_cast<uint16_t *>(ws2);
+        uint16_t *kb = reinterpret_cast<uint16_t *>(ws2 + align256(2 * size_t(nq)));
+        if (launch_cast_bf16(static_cast<const float *>(d_q), qb, nq, stream) != hipSuccess ||
+            launch_cast_bf16(static_cast<const float *>(d_k), kb, nkv, stream) != hipSuccess)
+            return SIFT_ERR_HIP;
+        q = qb;
+        k = kb;
+    }
+    const size_t rows = size_t(hl.Hq) * size_t(hl.G);
+    char *tb = ws + base;
+    int32_t *ca_prefix = reinterpret_cast<int32_t *>(tb);
+    int32_t *ca_list = reinterpret_cast<int32_t *>(tb + align256(4 * size_t(hl.Hq) * size_t(hl.ndocs > 0 ? hl.ndocs : 1)));
+    int32_t *rowinfo = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ca_list) + align256(4 * rows));
+    if (launch_bits_prepass(hl, pv, d_la, d_ca, ca_prefix, ca_list, rowinfo, stream) != hipSuccess ||
+        launch_transpose_v(hl, d_v, dtype == SIFT_FP32, vt, counters, stream) != hipSuccess ||
+        launch_prefill(hl, pv, q, k, vt, nullptr, nullptr, rowinfo, ca_list, d_la, scale, d_out, d_lse,
+                       counters, stream) != hipSuccess)
         return SIFT_ERR_HIP;
     return SIFT_OK;
 }

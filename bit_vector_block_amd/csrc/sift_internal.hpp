@@ -38,6 +38,7 @@ struct PlanView {
 struct HostLayout {
     int32_t R = 0, ndocs = 0, G = 0, Hq = 0, Hkv = 0, D = 0;
     int64_t la_words = 0, ca_words = 0, max_nnz = 0;
+    int64_t max_doc_tiles = 0;
     uint64_t fingerprint = 0;
     std::vector<int32_t> plan;  // the full plan image (header + arrays)
 };
@@ -55,14 +56,20 @@ size_t decode_workspace_bytes(const HostLayout &hl);
 hipError_t launch_decode(const HostLayout &hl, const PlanView &pv, const uint32_t *la,
                          const uint32_t *ca, int32_t *row_ptr, int32_t *col_idx, void *workspace,
                          hipStream_t stream);
+// Fused path (no CSR): per head, the request-level CA page lists and per-row list records.
+hipError_t launch_bits_prepass(const HostLayout &hl, const PlanView &pv, const uint32_t *la, const uint32_t *ca,
+                               int32_t *ca_prefix, int32_t *ca_list, int32_t *rowinfo, hipStream_t stream);
 hipError_t launch_cast_bf16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);
 // V [N][Hkv][D] (bf16, or fp32 when fp32 is set) -> bf16 V^T [Hkv][D][N] in the prefill layout;
 // also zeroes the 8 row-queue counters the attention kernel claims rows from.
 hipError_t launch_transpose_v(const HostLayout &hl, const void *v, bool fp32, uint16_t *vt, int *counters,
                               hipStream_t stream);
+// Attention over the CSR (rowinfo == nullptr) or, fused, over lists the kernel builds from the
+// pre-pass records, the CA page lists and the LA bits (row_ptr, col_idx unused).
 hipError_t launch_prefill(const HostLayout &hl, const PlanView &pv, const uint16_t *q,
                           const uint16_t *k, const uint16_t *vt, const int32_t *row_ptr,
-                          const int32_t *col_idx, float scale, float *out, float *lse, int *counters,
+                          const int32_t *col_idx, const int32_t *rowinfo, const int32_t *ca_list,
+                          const uint32_t *la_bits, float scale, float *out, float *lse, int *counters,
                           hipStream_t stream);
 
 }  // namespace sift

@@ -106,7 +106,7 @@ int64_t sift_ca_words(const sift_layout *layout);      /* uint32 words of all CA
 int64_t sift_csr_max_nnz(const sift_layout *layout);
 /* Bytes of the device plan written by sift_plan_upload. */
 size_t sift_plan_bytes(const sift_layout *layout);
-/* Bytes of device scratch that sift_decode_bits / sift_sparse_prefill need. */
+/* Bytes of device scratch that sift_decode_bits / sift_sparse_prefill / sift_sparse_prefill_bits need. */
 size_t sift_workspace_bytes(const sift_layout *layout, sift_dtype dtype);
 
 /*
@@ -158,6 +158,25 @@ sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan,
                                 const int32_t *d_row_ptr, const int32_t *d_col_idx, float scale,
                                 float *d_out, float *d_lse,
                                 void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sift_sparse_prefill_bits: the same attention, with the decode fused into it (no CSR).  The
+ * SIFT technical summary's "Design del Sistema" has the attention kernel read the bit vectors
+ * themselves; here a small pre-pass lists each request's CA-marked pages once per head (the
+ * CA part of every row of a document is a leading slice of that list), and each attention
+ * workgroup builds its rows' tile lists from that slice and from the row's own LA bits.
+ * d_la, d_ca: the layer's bits as for sift_decode_bits.  Other arguments, the output and the
+ * 16-byte alignment rule as for sift_sparse_prefill; the result is bit-identical to
+ * sift_decode_bits followed by sift_sparse_prefill on the same bits.
+ * d_workspace: >= sift_workspace_bytes(layout, dtype) bytes.
+ * Errors: SIFT_ERR_INVALID, SIFT_ERR_CAPACITY (workspace), SIFT_ERR_UNSUPPORTED (head_dim, tile,
+ * a document of more than 1984 tiles), SIFT_ERR_HIP.
+ */
+sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_plan,
+                                     const uint32_t *d_la, const uint32_t *d_ca,
+                                     const void *d_q, const void *d_k, const void *d_v, sift_dtype dtype,
+                                     float scale, float *d_out, float *d_lse,
+                                     void *d_workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *sift_status_string(sift_status status);

@@ -143,3 +143,23 @@ def test_empty_layout_sizes():
     lay = sift.Layout([0], [], [0], 2, 1, 64)
     assert lay.num_tiles == 0 and lay.num_rows == 0 and lay.csr_max_nnz == 0
     assert lay.plan_bytes > 0 and lay.workspace_bytes() > 0
+
+def test_prefill_bits_validation():
+    case = W.random_small_case(4, d=64)
+    lay = sift.Layout.from_case(case)
+    lib = sift.library()
+    vp = ctypes.c_void_p
+    a = vp(4096)
+    # null Q
+    st = lib.sift_sparse_prefill_bits(lay.ref, a, a, a, vp(0), a, a, B.SIFT_BF16, ctypes.c_float(0.0),
+                                      a, vp(0), a, 1 << 30, vp(0))
+    assert st == B.SIFT_ERR_INVALID
+    # workspace too small
+    st = lib.sift_sparse_prefill_bits(lay.ref, a, a, a, a, a, a, B.SIFT_BF16, ctypes.c_float(0.0),
+                                      a, vp(0), a, 16, vp(0))
+    assert st == B.SIFT_ERR_CAPACITY
+    # a document of more than 1984 tiles
+    big = sift.Layout([1], [1985 * 64], [0], 1, 1, 64)
+    st = lib.sift_sparse_prefill_bits(big.ref, a, a, a, a, a, a, B.SIFT_BF16, ctypes.c_float(0.0),
+                                      a, vp(0), a, 1 << 40, vp(0))
+    assert st == B.SIFT_ERR_UNSUPPORTED
