@@ -1,0 +1,100 @@
+"""Pins of the encoder oracle (oracle/encoder.py): closed forms, special cases, hand-worked
+selections and invariants."""
+import numpy as np
+import pytest
+
+from bit_vector_block_amd import workloads as W
+from oracle import encoder as E
+
+
+def _small(seed, **kw):
+    return W.random_small_case(seed, max_requests=2, max_docs=3, max_tiles=3, hq=2, hkv=1, d=16, **kw)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_masses_rows_sum_to_valid_query_count(seed):
+    case = _small(seed)
+    M = E.tile_masses(case)
+    valid = E.valid_tokens(case).reshape(-1, 64).sum(axis=1)
+    for h in range(case.num_q_heads):
+        assert np.allclose(M[h].sum(axis=1), valid, rtol=0, atol=1e-9)
+
+
+def test_masses_zero_queries_give_uniform_attention():
+    """Q = 0: every query attends uniformly to its valid causal keys, so a tile pair's mass is a
+    count ratio summed over the query tile (no softmax involved)."""
+    case = _small(7)
+    case.q[:] = 0
+    M = E.tile_masses(case)
+    tile_req, _, _, req_first, _, _ = E._segments(case)
+    valid = E.valid_tokens(case)
+    G = len(tile_req)
+    for g in range(G):
+        b = tile_req[g]
+        t0 = req_first[b]
+        for c in range(t0, g + 1):
+            want = 0.0
+            for qt in range(64 * g, 64 * g + 64):
+                if not valid[qt]:
+                    continue
+                keys = [kt for kt in range(64 * t0, qt + 1) if valid[kt]]
+                want += sum(1 for kt in keys if kt // 64 == c) / len(keys)
+            assert abs(M[0, g, c] - want) < 1e-9 and abs(M[1, g, c] - want) < 1e-9
+
+
+def test_masses_outside_request_or_future_are_zero():
+    case = _small(3)
+    M = E.tile_masses(case)
+    tile_req, *_ = E._segments(case)
+    G = len(tile_req)
+    for g in range(G):
+        for c in range(G):
+            if c > g or tile_req[c] != tile_req[g]:
+                assert M[:, g, c].max() == 0.0
+
+
+@pytest.mark.parametrize("masses,p,forced,want", [
+    ([0.5, 0.3, 0.2], 0.7, set(), {0, 1}),
+    ([0.2, 0.3, 0.5], 0.7, set(), {2, 1}),
+    ([0.25, 0.25, 0.25, 0.25], 0.5, set(), {0, 1}),
+    ([0.5, 0.5, 0.0], 1.0, set(), {0, 1}),
+    ([0.0, 0.0, 0.0], 0.9, {0}, {0}),
+    ([0.1, 0.6, 0.3], 0.5, {2, 0}, {1, 2, 0}),
+    ([1.0], 0.9, set(), {0}),
+])
+def test_select_top_p_hand_worked(masses, p, forced, want):
+    assert E.select_top_p(masses, p, forced) == want
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_select_top_p_is_the_minimal_sorted_prefix(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 65))
+    m = rng.random(n).astype(np.float32) ** 3
+    p = float(rng.uniform(0.1, 1.0))
+    keep = E.select_top_p(m, p, set())
+    order = sorted(range(n), key=lambda i: (-float(m[i]), i))
+    k = len(keep)
+    assert keep == set(order[:k])
+    tot = float(m.astype(np.float64).sum())
+    kept = float(m[order[:k]].astype(np.float64).sum())
+    # reaches the threshold (float32 scan: allow one rounding), and one fewer does not
+    assert kept >= p * tot * (1 - 1e-5) or k == n
+    if k > 1:
+        assert float(m[order[:k - 1]].astype(np.float64).sum()) < p * tot * (1 + 1e-5)
+
+
+def test_select_bits_forced_and_last_document():
+    case = _small(11)
+    M = E.tile_masses(case)
+    la, ca = E.select_bits(case, M, 0.5, 0.5)
+    tile_req, tile_doc, _, _, doc_first, doc_T = E._segments(case)
+    for d, (la_d, ca_d) in enumerate(zip(la, ca)):
+        T = doc_T[d]
+        for r in range(T):
+            assert la_d[:, r, r].all() and la_d[:, r, 0].all()
+            assert not la_d[:, r, r + 1:].any()
+        assert ca_d[:, 0].all()
+        b = tile_req[doc_first[d]]
+        if not any(tile_req[g] == b and tile_doc[g] > d for g in range(len(tile_req))):
+            assert ca_d[:, 1:].sum() == 0, "nothing attends to the last document's pages"
