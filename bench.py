@@ -134,6 +134,8 @@ def main(argv=None):
                     help="layers of the pipelined multi-layer run (per-layer bits from pinned host memory; 0: skip)")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the fused decode-in-attention timing (sift_sparse_prefill_bits)")
+    ap.add_argument("--no-encoder", action="store_true",
+                    help="skip the offline-encoder timing (tile masses of the dense attention + top-p bits)")
     ap.add_argument("--no-full-recompute", action="store_true",
                     help="skip the full-recompute comparison (same kernels on all-ones bits)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -325,6 +327,31 @@ def main(argv=None):
             "ms_per_layer": round(ms_pipe / L, 5),
             "vs_single_layer_step": round(ms_pipe / L / ms_per_step, 3),
             "note": "per-layer bits differ (same densities), H2D from pinned host one layer ahead; Q/K/V shared",
+        }
+    if not args.no_encoder:
+        # the offline encoder on the same layer: per-tile softmax mass of the dense causal
+        # attention (two score passes over every causal tile pair), then top-p LA/CA selection
+        log("offline encoder")
+        masses = sift.tile_masses(lay, q, k, plan=plan)
+        la_e, ca_e = sift.select_bits(lay, masses, 0.9, 0.9, plan=plan)
+        torch.cuda.synchronize()
+        reps = 3
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        for _ in range(reps):
+            sift.tile_masses(lay, q, k, plan=plan, masses=masses)
+        e1.record(stream)
+        for _ in range(reps):
+            sift.select_bits(lay, masses, 0.9, 0.9, plan=plan, la=la_e, ca=ca_e)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        ms_m, ms_s = e0.elapsed_time(e1) / reps, e1.elapsed_time(e2) / reps
+        causal_pairs = lay.csr_max_nnz  # all-ones bits: every causal tile pair of every q head
+        result["encoder"] = {
+            "ms_tile_masses": round(ms_m, 4),
+            "ms_select_bits": round(ms_s, 4),
+            "score_tflops": round(2.0 * causal_pairs * 2 * 64 * 64 * D / (ms_m * 1e-3) / 1e12, 3),
+            "note": "dense causal scores computed twice (row max/sum, then tile masses); top-p 0.9 / 0.9",
         }
     if args.cpu_seconds > 0:
         log(f"cpu baseline (~{args.cpu_seconds:.0f} s)")

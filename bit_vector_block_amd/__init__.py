@@ -1,15 +1,19 @@
 """bit_vector_block_amd: SIFT bit-vector sparse RAG prefill on MI355X (gfx950).
 
-Two hand-written HIP kernels behind the C ABI of include/sift.h:
+Hand-written HIP kernels behind the C ABI of include/sift.h:
   * ``decode_bits``    -- LA/CA bit vectors -> per-(head, query tile) CSR of KV tiles;
   * ``sparse_prefill`` -- block-sparse causal GQA attention over that CSR
                           (bf16 MFMA, online softmax, fp32 output);
-  * ``sparse_prefill_bits`` -- the same attention with the decode fused in (reads the bits).
+  * ``sparse_prefill_bits`` -- the same attention with the decode fused in (reads the bits);
+  * ``tile_masses`` / ``select_bits`` -- the offline encoder: per-tile softmax mass of the dense
+                          attention, then top-p selection into LA/CA bits.
 This package is the ctypes binding (argument marshalling), the seeded synthetic
 workloads in ``workloads`` and the multi-layer stream orchestration in ``pipeline``.
 """
 from ._binding import (SIFT_BF16, SIFT_FP32, Layout, SiftError, decode_bits, default_scale,
-                       library, plan_upload, sparse_prefill, sparse_prefill_bits)
+                       encode_masses_bytes, library, plan_upload, select_bits, sparse_prefill,
+                       sparse_prefill_bits, tile_masses)
 
 __all__ = ["Layout", "SiftError", "decode_bits", "sparse_prefill", "sparse_prefill_bits", "plan_upload",
-           "library", "default_scale", "SIFT_BF16", "SIFT_FP32"]
+           "tile_masses", "select_bits", "encode_masses_bytes", "library", "default_scale", "SIFT_BF16",
+           "SIFT_FP32"]

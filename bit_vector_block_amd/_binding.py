@@ -23,7 +23,7 @@ EXPORTED = (
     "sift_num_tiles", "sift_padded_tokens", "sift_num_rows", "sift_la_words", "sift_ca_words",
     "sift_csr_max_nnz", "sift_plan_bytes", "sift_workspace_bytes", "sift_plan_upload",
     "sift_decode_bits", "sift_sparse_prefill", "sift_sparse_prefill_bits", "sift_status_string",
-    "sift_abi_version",
+    "sift_abi_version", "sift_encode_masses_bytes", "sift_tile_masses", "sift_select_bits",
 )
 
 
@@ -76,6 +76,12 @@ def _lib():
     lib.sift_sparse_prefill_bits.argtypes = [L, vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_float,
                                              vp, vp, vp, sz, vp]
     lib.sift_sparse_prefill_bits.restype = ctypes.c_int
+    lib.sift_encode_masses_bytes.argtypes = [L]
+    lib.sift_encode_masses_bytes.restype = sz
+    lib.sift_tile_masses.argtypes = [L, vp, vp, vp, ctypes.c_float, vp, sz, vp]
+    lib.sift_tile_masses.restype = ctypes.c_int
+    lib.sift_select_bits.argtypes = [L, vp, vp, sz, ctypes.c_float, ctypes.c_float, vp, vp, vp]
+    lib.sift_select_bits.restype = ctypes.c_int
     lib.sift_status_string.argtypes = [ctypes.c_int]
     lib.sift_status_string.restype = ctypes.c_char_p
     lib.sift_abi_version.argtypes = []
@@ -265,6 +271,59 @@ def sparse_prefill_bits(layout: Layout, la, ca, q, k, v, plan=None, scale: Optio
         ctypes.c_void_p(lse.data_ptr() if lse is not None else 0), ctypes.c_void_p(ws.data_ptr()), ws_bytes,
         _stream_handle(torch, device)), "sift_sparse_prefill_bits")
     return out, (lse if want_lse else None)
+
+
+def encode_masses_bytes(layout: Layout) -> int:
+    return int(_lib().sift_encode_masses_bytes(layout.ref))
+
+
+def tile_masses(layout: Layout, q, k, plan=None, scale: Optional[float] = None, masses=None):
+    """Per-tile softmax mass of the dense causal attention (offline encoder, first step).
+
+    q [N,Hq,D], k [N,Hkv,D] bfloat16.  Returns fp32 masses [Hq, G, RT] (RT = the largest
+    request's tile count); entry (h, g, c - first tile of g's request) for the causal c <= g.
+    """
+    import torch
+    device = q.device
+    n, hq, hkv, d = layout.padded_tokens, layout.num_q_heads, layout.num_kv_heads, layout.head_dim
+    for name, t, shape in (("q", q, (n, hq, d)), ("k", k, (n, hkv, d))):
+        if tuple(t.shape) != shape or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device != device:
+            raise ValueError(f"{name}: need a contiguous bfloat16 tensor of shape {shape} on {device}")
+    if plan is None:
+        plan = plan_upload(layout, device)
+    nbytes = encode_masses_bytes(layout)
+    if masses is None:
+        rt = max(nbytes // (4 * max(hq * layout.num_tiles, 1)), 1)
+        masses = torch.empty((hq, layout.num_tiles, rt), dtype=torch.float32, device=device)
+    sc = 0.0 if scale is None else float(scale)
+    _check(_lib().sift_tile_masses(
+        layout.ref, ctypes.c_void_p(plan.data_ptr()), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+        ctypes.c_float(sc), ctypes.c_void_p(masses.data_ptr()), masses.numel() * masses.element_size(),
+        _stream_handle(torch, device)), "sift_tile_masses")
+    return masses
+
+
+def select_bits(layout: Layout, masses, p_la: float = 0.9, p_ca: float = 0.9, plan=None, la=None, ca=None):
+    """LA / CA words (int32 device tensors, layout as for decode_bits) from tile masses by top-p."""
+    import torch
+    device = masses.device
+    if masses.dtype != torch.float32 or not masses.is_contiguous():
+        raise ValueError("masses: need a contiguous float32 tensor (from tile_masses)")
+    if plan is None:
+        plan = plan_upload(layout, device)
+    if la is None:
+        la = torch.empty(max(layout.la_words, 1), dtype=torch.int32, device=device)
+    if ca is None:
+        ca = torch.empty(max(layout.ca_words, 1), dtype=torch.int32, device=device)
+    for name, t, words in (("la", la, layout.la_words), ("ca", ca, layout.ca_words)):
+        if t.dtype != torch.int32 or t.device != device or t.numel() < max(words, 1):
+            raise ValueError(f"{name}: need an int32 tensor of >= {words} words on {device}")
+    _check(_lib().sift_select_bits(
+        layout.ref, ctypes.c_void_p(plan.data_ptr()), ctypes.c_void_p(masses.data_ptr()),
+        masses.numel() * masses.element_size(), ctypes.c_float(p_la), ctypes.c_float(p_ca),
+        ctypes.c_void_p(la.data_ptr()), ctypes.c_void_p(ca.data_ptr()), _stream_handle(torch, device)),
+        "sift_select_bits")
+    return la, ca
 
 
 def default_scale(head_dim: int) -> float:

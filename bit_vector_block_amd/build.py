@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["sift_api.hip", "decode_kernels.hip", "prefill_kernels.hip"]
+SOURCES = ["sift_api.hip", "decode_kernels.hip", "prefill_kernels.hip", "encode_kernels.hip"]
 OUT = os.path.join(HERE, "libsift.so")
 
 HIPCC_FLAGS = [

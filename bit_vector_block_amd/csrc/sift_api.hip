@@ -67,6 +67,7 @@ sift_status build_layout(const sift_layout *layout, HostLayout *out) {
                 ca_words += static_cast<int64_t>(L.num_q_heads) * ceil_div(T, 32);
             }
             tb += ceil_div(L.question_len[b], kTile);
+            if (tb > hl.max_req_tiles) hl.max_req_tiles = tb;
             G += tb;
             max_nnz += tb * (tb + 1) / 2;
         }
@@ -391,6 +392,49 @@ sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_pl
         launch_transpose_v(hl, d_v, dtype == SIFT_FP32, vt, counters, stream) != hipSuccess ||
         launch_prefill(hl, pv, q, k, vt, nullptr, nullptr, rowinfo, ca_list, d_la, scale, d_out, d_lse,
                        counters, stream) != hipSuccess)
+        return SIFT_ERR_HIP;
+    return SIFT_OK;
+}
+
+size_t sift_encode_masses_bytes(const sift_layout *layout) {
+    HostLayout hl;
+    if (build_layout(layout, &hl) != SIFT_OK) return 0;
+    return sizeof(float) * size_t(hl.Hq) * size_t(hl.G) * size_t(hl.max_req_tiles > 0 ? hl.max_req_tiles : 1);
+}
+
+sift_status sift_tile_masses(const sift_layout *layout, const void *d_plan, const void *d_q, const void *d_k,
+                             float scale, float *d_masses, size_t masses_bytes, hipStream_t stream) {
+    HostLayout hl;
+    sift_status st = build_layout(layout, &hl);
+    if (st != SIFT_OK) return st;
+    if (hl.G == 0) return SIFT_OK;
+    if (!d_plan || !d_q || !d_k || !d_masses) return SIFT_ERR_INVALID;
+    auto aligned16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if (!aligned16(d_q) || !aligned16(d_k)) return SIFT_ERR_INVALID;
+    if (!(scale > 0.0f)) scale = 1.0f / sqrtf(float(hl.D));
+    if (!isfinite(scale)) return SIFT_ERR_INVALID;
+    if (masses_bytes < sift_encode_masses_bytes(layout)) return SIFT_ERR_CAPACITY;
+    const PlanView pv = plan_view(hl, d_plan);
+    if (launch_tile_masses(hl, pv, static_cast<const uint16_t *>(d_q), static_cast<const uint16_t *>(d_k), scale,
+                           d_masses, static_cast<int>(hl.max_req_tiles), stream) != hipSuccess)
+        return SIFT_ERR_HIP;
+    return SIFT_OK;
+}
+
+sift_status sift_select_bits(const sift_layout *layout, const void *d_plan, const float *d_masses,
+                             size_t masses_bytes, float p_la, float p_ca, uint32_t *d_la, uint32_t *d_ca,
+                             hipStream_t stream) {
+    HostLayout hl;
+    sift_status st = build_layout(layout, &hl);
+    if (st != SIFT_OK) return st;
+    if (hl.ndocs == 0) return SIFT_OK;
+    if (!d_plan || !d_masses || (hl.la_words > 0 && !d_la) || (hl.ca_words > 0 && !d_ca)) return SIFT_ERR_INVALID;
+    if (!(p_la > 0.0f && p_la <= 1.0f) || !(p_ca > 0.0f && p_ca <= 1.0f)) return SIFT_ERR_INVALID;
+    if (hl.max_doc_tiles > 64) return SIFT_ERR_UNSUPPORTED;  // one lane per candidate tile
+    if (masses_bytes < sift_encode_masses_bytes(layout)) return SIFT_ERR_CAPACITY;
+    const PlanView pv = plan_view(hl, d_plan);
+    if (launch_select_bits(hl, pv, d_masses, static_cast<int>(hl.max_req_tiles), p_la, p_ca, d_la, d_ca, stream) !=
+        hipSuccess)
         return SIFT_ERR_HIP;
     return SIFT_OK;
 }

@@ -39,6 +39,7 @@ struct HostLayout {
     int32_t R = 0, ndocs = 0, G = 0, Hq = 0, Hkv = 0, D = 0;
     int64_t la_words = 0, ca_words = 0, max_nnz = 0;
     int64_t max_doc_tiles = 0;
+    int64_t max_req_tiles = 0;
     uint64_t fingerprint = 0;
     std::vector<int32_t> plan;  // the full plan image (header + arrays)
 };
@@ -59,6 +60,11 @@ hipError_t launch_decode(const HostLayout &hl, const PlanView &pv, const uint32_
 // Fused path (no CSR): per head, the request-level CA page lists and per-row list records.
 hipError_t launch_bits_prepass(const HostLayout &hl, const PlanView &pv, const uint32_t *la, const uint32_t *ca,
                                int32_t *ca_prefix, int32_t *ca_list, int32_t *rowinfo, hipStream_t stream);
+// Offline encoder (tile masses of dense attention, then top-p selection into LA/CA words).
+hipError_t launch_tile_masses(const HostLayout &hl, const PlanView &pv, const uint16_t *q, const uint16_t *k,
+                              float scale, float *masses, int RT, hipStream_t stream);
+hipError_t launch_select_bits(const HostLayout &hl, const PlanView &pv, const float *masses, int RT, float p_la,
+                              float p_ca, uint32_t *la_out, uint32_t *ca_out, hipStream_t stream);
 hipError_t launch_cast_bf16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);
 // V [N][Hkv][D] (bf16, or fp32 when fp32 is set) -> bf16 V^T [Hkv][D][N] in the prefill layout;
 // also zeroes the 8 row-queue counters the attention kernel claims rows from.

@@ -178,6 +178,34 @@ sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_pl
                                      float scale, float *d_out, float *d_lse,
                                      void *d_workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Offline encoder.  The SIFT technical summary's "Design del Sistema" computes the bits offline
+ * from a dense prefill of each document, keeping the positions with high attention scores; the
+ * pages leave the selection rule open.  This encoder reads it as a top-p rule on tile masses:
+ *
+ * sift_tile_masses: mass(h, g, c) = sum, over the valid queries of query tile g and the keys of
+ * key tile c, of the softmax probability of the dense causal attention of the request (bf16
+ * Q [N][Hq][D] and K [N][Hkv][D], 16-byte aligned; scale <= 0 selects 1/sqrt(head_dim)).
+ * d_masses: fp32 [Hq][G][RT], RT = the largest request's tile count; entry (h, g, c - first)
+ * with first = the first tile of g's request, written for first <= c <= g only.  masses_bytes >=
+ * sift_encode_masses_bytes(layout).
+ *
+ * sift_select_bits: LA row r of document d keeps its candidate tiles c <= r by decreasing mass
+ * (ties: smaller c) up to the first prefix whose mass reaches p_la of their total, plus tiles r
+ * and 0; CA page c of d gets the mass that the request's later documents' query tiles put on it
+ * (summed in increasing tile order) and the pages are kept the same way with p_ca, plus page 0.
+ * The threshold test sums in float32 in a fixed order (an inclusive Hillis-Steele scan of the
+ * sorted masses).  Writes every word of d_la / d_ca (layout as for sift_decode_bits).
+ * Errors: SIFT_ERR_INVALID (p outside (0, 1], nulls), SIFT_ERR_CAPACITY (masses_bytes),
+ * SIFT_ERR_UNSUPPORTED (a document of more than 64 tiles), SIFT_ERR_HIP.
+ */
+size_t sift_encode_masses_bytes(const sift_layout *layout);
+sift_status sift_tile_masses(const sift_layout *layout, const void *d_plan, const void *d_q, const void *d_k,
+                             float scale, float *d_masses, size_t masses_bytes, hipStream_t stream);
+sift_status sift_select_bits(const sift_layout *layout, const void *d_plan, const float *d_masses,
+                             size_t masses_bytes, float p_la, float p_ca, uint32_t *d_la, uint32_t *d_ca,
+                             hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *sift_status_string(sift_status status);
 

@@ -111,6 +111,32 @@ def tile_masses(case, scale=None):
     return M
 
 
+def tile_mass_row(case, h, g, scale=None):
+    """fp64 masses M[h, g, :] of one query tile: the definition of tile_masses evaluated for the
+    64 queries of tile g only (so that full-size workloads can be checked on sampled rows)."""
+    tile_req, _, _, req_first, _, _ = _segments(case)
+    G = len(tile_req)
+    t0 = int(req_first[tile_req[g]])
+    kvh = h // (case.num_q_heads // case.num_kv_heads)
+    sc = 1.0 / np.sqrt(case.head_dim) if scale is None else scale
+    s0, q0, s1 = t0 * TILE, g * TILE, (g + 1) * TILE
+    q = _values(case, case.q[q0:s1, h, :])
+    k = _values(case, case.k[s0:s1, kvh, :])
+    valid = valid_tokens(case)
+    q_tok = np.arange(q0, s1)
+    k_tok = np.arange(s0, s1)
+    allowed = (k_tok[None, :] <= q_tok[:, None]) & valid[s0:s1][None, :] & valid[q0:s1][:, None]
+    s = np.where(allowed, (q @ k.T) * sc, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    mx = np.where(np.isfinite(mx), mx, 0.0)
+    p = np.exp(s - mx)
+    l = p.sum(axis=1, keepdims=True)
+    p = np.divide(p, l, out=np.zeros_like(p), where=l > 0)
+    out = np.zeros(G)
+    out[t0:g + 1] = p.reshape(TILE, g + 1 - t0, TILE).sum(axis=(0, 2))
+    return out
+
+
 def _scan64(v):
     """Inclusive Hillis-Steele scan of 64 float32 values (each round adds the value `off` slots
     back, all slots at once)."""

@@ -163,3 +163,27 @@ def test_prefill_bits_validation():
     st = lib.sift_sparse_prefill_bits(big.ref, a, a, a, a, a, a, B.SIFT_BF16, ctypes.c_float(0.0),
                                       a, vp(0), a, 1 << 40, vp(0))
     assert st == B.SIFT_ERR_UNSUPPORTED
+
+
+def test_encoder_validation():
+    case = W.random_small_case(4, d=64)
+    lay = sift.Layout.from_case(case)
+    lib = sift.library()
+    vp, f = ctypes.c_void_p, ctypes.c_float
+    a = vp(4096)
+    need = lib.sift_encode_masses_bytes(lay.ref)
+    tiles = [-(-int(n) // 64) for n in case.doc_len]
+    rt, d0 = 0, 0
+    for b, k in enumerate(case.req_num_docs):
+        rt = max(rt, sum(tiles[d0:d0 + k]) + -(-int(case.question_len[b]) // 64))
+        d0 += k
+    assert need == 4 * lay.num_q_heads * lay.num_tiles * rt
+    assert lib.sift_tile_masses(lay.ref, a, vp(0), a, f(0.0), a, need, vp(0)) == B.SIFT_ERR_INVALID
+    assert lib.sift_tile_masses(lay.ref, a, vp(4104), a, f(0.0), a, need, vp(0)) == B.SIFT_ERR_INVALID
+    assert lib.sift_tile_masses(lay.ref, a, a, a, f(0.0), a, need - 4, vp(0)) == B.SIFT_ERR_CAPACITY
+    for p_la, p_ca in ((0.0, 0.5), (0.5, 1.5), (float("nan"), 0.5)):
+        assert lib.sift_select_bits(lay.ref, a, a, need, f(p_la), f(p_ca), a, a, vp(0)) == B.SIFT_ERR_INVALID
+    assert lib.sift_select_bits(lay.ref, a, a, need - 4, f(0.9), f(0.9), a, a, vp(0)) == B.SIFT_ERR_CAPACITY
+    big = sift.Layout([1], [65 * 64], [0], 1, 1, 64)
+    nb = lib.sift_encode_masses_bytes(big.ref)
+    assert lib.sift_select_bits(big.ref, a, a, nb, f(0.9), f(0.9), a, a, vp(0)) == B.SIFT_ERR_UNSUPPORTED

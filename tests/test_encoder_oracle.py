@@ -98,3 +98,17 @@ def test_select_bits_forced_and_last_document():
         b = tile_req[doc_first[d]]
         if not any(tile_req[g] == b and tile_doc[g] > d for g in range(len(tile_req))):
             assert ca_d[:, 1:].sum() == 0, "nothing attends to the last document's pages"
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_mass_row_sums_to_the_valid_query_count_and_matches_the_full_matrix(seed):
+    """The one-row evaluation: each query's probabilities sum to one (so the row sums to the
+    tile's valid query count), and it agrees with the whole-request evaluation."""
+    case = _small(20 + seed)
+    M = E.tile_masses(case)
+    valid = E.valid_tokens(case).reshape(-1, 64).sum(axis=1)
+    for h in range(case.num_q_heads):
+        for g in range(M.shape[1]):
+            row = E.tile_mass_row(case, h, g)
+            assert abs(row.sum() - valid[g]) < 1e-9
+            assert np.allclose(row, M[h, g], rtol=0, atol=1e-12)
