@@ -104,7 +104,7 @@ def test_select_bits_forced_and_last_document():
 def test_mass_row_sums_to_the_valid_query_count_and_matches_the_full_matrix(seed):
     """The one-row evaluation: each query's probabilities sum to one (so the row sums to the
     tile's valid query count), and it agrees with the whole-request evaluation."""
-    case = _small(20 + seed)
+    case = W.random_small_case(20 + seed, max_requests=2, max_docs=3, max_tiles=3, hq=4, hkv=2, d=16)
     M = E.tile_masses(case)
     valid = E.valid_tokens(case).reshape(-1, 64).sum(axis=1)
     for h in range(case.num_q_heads):
@@ -112,3 +112,59 @@ def test_mass_row_sums_to_the_valid_query_count_and_matches_the_full_matrix(seed
             row = E.tile_mass_row(case, h, g)
             assert abs(row.sum() - valid[g]) < 1e-9
             assert np.allclose(row, M[h, g], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_masses_equal_sdpa_probabilities(seed):
+    """torch's scaled_dot_product_attention (fp64, CPU) with V = the identity returns the softmax
+    probability matrix itself.  The GQA map repeats each KV head over its q heads, and the mask is
+    causal over the valid keys.  Summed over 64 x 64 blocks, these must be the oracle's masses."""
+    import torch
+    case = W.random_small_case(40 + seed, max_requests=2, max_docs=3, max_tiles=3, hq=4, hkv=2, d=16)
+    M = E.tile_masses(case)
+    tile_req, _, _, req_first, _, _ = E._segments(case)
+    valid = torch.from_numpy(E.valid_tokens(case))
+    q = torch.from_numpy(W.bf16_bits_to_f32(case.q).astype(np.float64))
+    k = torch.from_numpy(W.bf16_bits_to_f32(case.k).astype(np.float64))
+    group = case.num_q_heads // case.num_kv_heads
+    for b in range(len(case.req_num_docs)):
+        t0 = int(req_first[b])
+        nt = int((tile_req == b).sum())
+        s0, s1 = 64 * t0, 64 * (t0 + nt)
+        n = s1 - s0
+        qb = q[s0:s1].permute(1, 0, 2)
+        kb = k[s0:s1].permute(1, 0, 2).repeat_interleave(group, dim=0)
+        vb = torch.eye(n, dtype=torch.float64).expand(case.num_q_heads, n, n)
+        ok = valid[s0:s1]
+        mask = torch.tril(torch.ones(n, n, dtype=torch.bool)) & ok[None, :]
+        mask |= ~ok[:, None]  # padded queries: any non-empty row (zeroed below)
+        p = torch.nn.functional.scaled_dot_product_attention(qb, kb, vb, attn_mask=mask)
+        p[:, ~ok, :] = 0.0
+        want = p.reshape(case.num_q_heads, nt, 64, nt, 64).sum(dim=(2, 4)).numpy()
+        assert np.allclose(M[:, t0:t0 + nt, t0:t0 + nt], want, rtol=0, atol=1e-10)
+
+
+def test_select_bits_hand_worked():
+    """Two documents of 3 and 2 tiles, one question tile, one head; dyadic masses (exact in
+    float32), p_la = 0.5, p_ca = 0.4.  Worked by hand:
+      doc 0, LA row 1: 0.625 | 0.375 -> c0 reaches 0.5 -> {0}, plus the diagonal -> {0, 1};
+      doc 0, LA row 2: 0.125 | 0.25 | 0.625 -> c2 alone reaches 0.5 -> {2}, plus tile 0 -> {0, 2};
+      doc 0, CA: the later document's query tiles 3 and 4 give pages 0.25 | 0.625 | 0.75
+                 (total 1.625, threshold 0.65): page 2 alone reaches it -> {2} plus page 0;
+                 the question tile (2.0 on page 1) and doc 0's own rows do not count;
+      doc 1: rows of at most two tiles are all forced; its CA pages have no reader -> {0}."""
+    case = W.make_case("hand", 1, [2], [192, 128], [64], 1, 1, 64, np.full((1, 1), 0.5), np.full((1, 1), 0.5))
+    M = np.zeros((1, 6, 6))
+    M[0, 0, 0] = 3.0
+    M[0, 1, :2] = [0.625, 0.375]
+    M[0, 2, :3] = [0.125, 0.25, 0.625]
+    M[0, 3, :4] = [0.125, 0.5, 0.25, 0.125]
+    M[0, 4, :5] = [0.125, 0.125, 0.5, 0.25, 0.75]
+    M[0, 5, :6] = [0.0, 2.0, 0.0, 0.5, 0.5, 1.0]
+    la, ca = E.select_bits(case, M, 0.5, 0.4)
+    want_la0 = np.array([[1, 0, 0], [1, 1, 0], [1, 0, 1]], bool)
+    want_la1 = np.array([[1, 0], [1, 1]], bool)
+    np.testing.assert_array_equal(la[0][0], want_la0)
+    np.testing.assert_array_equal(la[1][0], want_la1)
+    np.testing.assert_array_equal(ca[0][0], [True, False, True])
+    np.testing.assert_array_equal(ca[1][0], [True, False])
