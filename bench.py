@@ -15,7 +15,10 @@ divided by the step time.  The roofline block reports the sparse_prefill call
 bf16 dense MFMA peak, timed with HIP events on the stream it runs on; the
 full-recompute block runs the same two calls on all-ones bits (dense causal
 attention per request), the pages' speed reference.  The CPU baseline is the
-fp64 oracle on a bounded sample of rows.
+fp64 oracle on a bounded sample of rows.  Also reported: the bf16 MFMA rate of a
+register-only MFMA loop measured on the same GPU (libsift_probe.so) and the
+prefill's share of it; "useful" FLOPs (valid causal (query, key) pairs only);
+and the size of the bits against the documents' bf16 K/V of one layer.
 """
 from __future__ import annotations
 
@@ -76,6 +79,61 @@ def profiled_traffic(workload):
                     hashlib.sha256(src).hexdigest()[:16] == info["source_sha256_16"]:
                 return int(info["hbm_bytes_per_launch"])
     return None
+
+
+def tile_valid_counts(case):
+    """Valid tokens of every 64-token tile, in the padded layout (documents, then the question,
+    request after request)."""
+    out = []
+    d = 0
+    for b, k in enumerate(case.req_num_docs):
+        lens = [int(case.doc_len[d + i]) for i in range(int(k))] + [int(case.question_len[b])]
+        d += int(k)
+        for n in lens:
+            t = -(-n // 64)
+            out.extend(min(64, n - 64 * i) for i in range(t))
+    return np.array(out, dtype=np.int64)
+
+
+def useful_pairs(case, row_ptr, col_idx):
+    """(query, key) pairs that the listed tiles really contribute: valid queries x valid keys, and
+    on the diagonal tile only keys at or before the query.  A full off-diagonal tile is 64 x 64,
+    a full diagonal tile 64 x 65 / 2."""
+    tv = tile_valid_counts(case)
+    G = tv.size
+    rows = np.repeat(np.arange(row_ptr.size - 1), np.diff(row_ptr))
+    g = rows % G
+    t = col_idx[: row_ptr[-1]].astype(np.int64)
+    qv, kv = tv[g], tv[t]
+    qi = np.arange(64)
+    diag = np.array([[np.minimum(qi[:a] + 1, b).sum() for b in range(65)] for a in range(65)])
+    return int(np.where(t == g, diag[qv, kv], qv * kv).sum())
+
+
+def measured_mfma_peak(torch, dev, stream):
+    """bf16 MFMA TFLOP/s of a register-only MFMA loop on every CU (libsift_probe.so)."""
+    import ctypes
+    path = os.path.join(ROOT, "bit_vector_block_amd", "libsift_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.sift_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sift_probe_mfma_bf16.restype = ctypes.c_int
+    lib.sift_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.sift_probe_mfma_bf16_flops.restype = ctypes.c_double
+    wgs, iters, reps = 1024, 8000, 5   # four 4-wave workgroups per CU
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    h = ctypes.c_void_p(stream.cuda_stream)
+    for _ in range(2):
+        if lib.sift_probe_mfma_bf16(wgs, iters, ctypes.c_void_p(sink.data_ptr()), h) != 0:
+            raise RuntimeError("MFMA probe launch failed")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        lib.sift_probe_mfma_bf16(wgs, iters, ctypes.c_void_p(sink.data_ptr()), h)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return lib.sift_probe_mfma_bf16_flops(wgs, iters) / (ms * 1e-3) / 1e12, ms
 
 
 def cpu_baseline(case, row_ptr, target_seconds, seed=0):
@@ -219,9 +277,15 @@ def main(argv=None):
                 float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
                 float(np.mean([e[1].elapsed_time(e[2]) for e in evs])))
 
+    log("measured MFMA peak")
+    peak_meas, _ = measured_mfma_peak(torch, dev, stream)
     log(f"warmup {args.warmup}, timing {args.steps} steps")
     nnz, ms_per_step, decode_ms, prefill_ms = timed(la, ca, args.steps, args.warmup)
     rp_host = row_ptr.cpu().numpy().astype(np.int64)
+    useful = 4.0 * D * useful_pairs(case, rp_host, col_idx.cpu().numpy())
+    doc_tokens_padded = int(sum(64 * (-(-int(n) // 64)) for n in case.doc_len))
+    bits_bytes = 4 * (lay.la_words + lay.ca_words)
+    kv_doc_bytes = 2 * doc_tokens_padded * Hkv * D * 2  # bf16 K and V of the documents, one layer
 
     flops = float(nnz) * 4.0 * 64 * 64 * D
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -256,6 +320,19 @@ def main(argv=None):
         "decode_gbs": round(decode_bytes / (decode_ms * 1e-3) / 1e9, 1),
         "prefill_ms": round(prefill_ms, 5),
         "pct_bf16_peak_step": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "mfma_peak_measured_tflops": round(peak_meas, 1),
+        "prefill_pct_measured_peak": round(100.0 * achieved / peak_meas, 2),
+        "useful": {
+            "gflop_per_layer": round(useful / 1e9, 3),
+            "tflops_step": round(useful / (ms_per_step * 1e-3) / 1e12, 3),
+            "tflops_prefill": round(useful / (prefill_ms * 1e-3) / 1e12, 3),
+            "note": "valid (query, key) pairs only: diagonal tiles at 65/128, padded queries and keys removed",
+        },
+        "bits_vs_kv": {
+            "bits_bytes": int(bits_bytes),
+            "doc_kv_bytes": int(kv_doc_bytes),
+            "ratio": round(kv_doc_bytes / max(bits_bytes, 1), 1),
+        },
         "roofline": {
             "kernel": f"sift_sparse_prefill call: transpose_v_kernel + sparse_prefill_kernel<{D}>",
             "bound": "mfma",

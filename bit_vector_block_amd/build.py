@@ -10,6 +10,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["sift_api.hip", "decode_kernels.hip", "prefill_kernels.hip", "encode_kernels.hip"]
 OUT = os.path.join(HERE, "libsift.so")
+# the MFMA throughput probe bench.py measures the attention kernel against (not the prefill path)
+PROBE_SOURCES = ["mfma_probe.hip"]
+PROBE_OUT = os.path.join(HERE, "libsift_probe.so")
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
@@ -23,9 +26,9 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
+def _compile(sources, out, verbose):
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", OUT + ".tmp"]
+           *[os.path.join(CSRC, s) for s in sources], "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -35,7 +38,12 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(OUT + ".tmp", OUT)
+    os.replace(out + ".tmp", out)
+
+
+def build(verbose: bool = False) -> str:
+    _compile(SOURCES, OUT, verbose)
+    _compile(PROBE_SOURCES, PROBE_OUT, verbose)
     return OUT
 
 
