@@ -12,9 +12,10 @@
 //                   documents (summed in increasing tile order), the shortest prefix reaching
 //                   p_ca of the total, plus page 0.
 //
-// tile_mass_kernel   one workgroup per (q head, query tile), two passes over the row's causal
-//                    key tiles: the row max and sum of every query, then every tile's mass
-//                    (bf16 MFMA scores, fp32 softmax, deterministic reductions);
+// tile_mass_kernel   one workgroup per (KV head, group of up to four of its q heads, query tile),
+//                    two passes over the row's causal key tiles: the row max and sum of every
+//                    query, then every tile's mass (bf16 MFMA scores, fp32 softmax,
+//                    deterministic reductions); each K tile is loaded once for the group;
 // select_bits_kernel one wavefront per (q head, document): bitonic sort of the candidates, an
 //                    inclusive Hillis-Steele scan (the order in which the threshold test sums),
 //                    the cut, and the bit packing in LDS.
@@ -29,7 +30,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kEncThreads = 256;
 
 __device__ inline bool plan_ok(const PlanView &pv) {
     return pv.header[0] == static_cast<int32_t>(kPlanMagic) &&
@@ -57,38 +57,59 @@ __device__ inline f32x16 scores(const bf16x8 (&qf)[D / 16], const char *Kt, int 
     return s;
 }
 
-template <int D>
-__device__ inline void load_k_rows(char *Kt, const uint16_t *__restrict__ k, int64_t tok0, int Hkv, int kvh,
-                                   int tid) {
-    constexpr int CH = D / 8, KROW = 2 * D + 16;
-    for (int x = tid; x < 64 * CH; x += kEncThreads) {
-        const int r = x / CH, c = x % CH;
-        const uint4 w = *reinterpret_cast<const uint4 *>(k + ((tok0 + r) * Hkv + kvh) * D + 8 * c);
-        *reinterpret_cast<uint4 *>(Kt + r * KROW + 16 * c) = w;
-    }
-}
-
 __device__ inline float wave_sum(float x) {  // fixed butterfly order: deterministic
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
     return x;
 }
 
-template <int D>
-__global__ __launch_bounds__(kEncThreads) void tile_mass_kernel(PlanView pv, const uint16_t *__restrict__ q,
-                                                                 const uint16_t *__restrict__ k, int Hq, int Hkv,
-                                                                 float scale_log2, float *__restrict__ masses,
-                                                                 int RT) {
+// K tile c of KV head kvh -> this thread's 64 * D / 8 / NT sixteen-byte chunks, and back out to an
+// LDS tile with rows of 2 D + 16 bytes
+template <int D, int NT>
+__device__ __forceinline__ void stage_k_tile(uint4 (&stage)[64 * (D / 8) / NT], const uint16_t *__restrict__ k, int c,
+                                             int Hkv, int kvh, int tid) {
+    constexpr int CH = D / 8;
+#pragma unroll
+    for (int j = 0; j < 64 * CH / NT; ++j) {
+        const int x = tid + j * NT, r = x / CH, ch = x % CH;
+        stage[j] = *reinterpret_cast<const uint4 *>(k + ((static_cast<int64_t>(c) * kTile + r) * Hkv + kvh) * D + 8 * ch);
+    }
+}
+template <int D, int NT>
+__device__ __forceinline__ void store_k_tile(const uint4 (&stage)[64 * (D / 8) / NT], char *Kt, int tid) {
+    constexpr int CH = D / 8, KROW = 2 * D + 16;
+#pragma unroll
+    for (int j = 0; j < 64 * CH / NT; ++j) {
+        const int x = tid + j * NT, r = x / CH, ch = x % CH;
+        *reinterpret_cast<uint4 *>(Kt + r * KROW + 16 * ch) = stage[j];
+    }
+}
+
+// One workgroup per (KV head, group of HPW q heads of it, query tile g): 2 HPW wavefronts, wave w
+// takes q head (group base + w / 2) and queries 32 (w % 2) .. + 31, against all 64 keys of every
+// key tile.  The K tile is loaded once for the HPW heads that share it (GQA) and staged one tile
+// ahead in registers.  Pass 1: each query's running max and sum of exp2; pass 2: each tile's mass.
+template <int D, int HPW>
+__device__ __forceinline__ void tile_mass_body(const PlanView &pv, const uint16_t *__restrict__ q,
+                                               const uint16_t *__restrict__ k, int Hq, int Hkv, float scale_log2,
+                                               float *__restrict__ masses, int RT) {
+    constexpr int NT = 128 * HPW;
     constexpr int KROW = 2 * D + 16;
-    __shared__ __attribute__((aligned(16))) char Kt[64 * KROW];
-    __shared__ float ml[2][2][32][2];  // [qh][kh][query][m, l]
-    __shared__ float part[4];
+    constexpr int CH = D / 8;              // 16-byte chunks per key row
+    constexpr int PER = 64 * CH / NT;      // chunks each thread stages per tile
+    static_assert(PER * NT == 64 * CH, "tile chunks split evenly");
+    __shared__ __attribute__((aligned(16))) char Kt[2][64 * KROW];
+    __shared__ float part[2][2 * HPW];
     if (!plan_ok(pv)) return;
     const int G = pv.num_tiles;
-    const int h = blockIdx.x / G, g = blockIdx.x % G;
-    const int kvh = h / (Hq / Hkv);
+    const int group = Hq / Hkv, ngroups = group / HPW;
+    // latest query tiles (the longest rows) first
+    const int g = G - 1 - static_cast<int>(blockIdx.x / (Hkv * ngroups));
+    const int rest = static_cast<int>(blockIdx.x % (Hkv * ngroups));
+    const int kvh = rest / ngroups;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    const int qh = wave & 1, kh = wave >> 1, qi = 32 * qh + l32;
+    const int h = kvh * group + (rest % ngroups) * HPW + (wave >> 1);
+    const int qi = 32 * (wave & 1) + l32;
     const int first = pv.req_first[req_of_tile(pv, g)];
     const int q_valid = pv.tile_valid[g];
     bf16x8 qf[D / 16];
@@ -97,71 +118,104 @@ __global__ __launch_bounds__(kEncThreads) void tile_mass_kernel(PlanView pv, con
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc) qf[dc] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * dc);
     }
-    auto masked = [&](f32x16 &s, int c) {
-        const int kv_valid = pv.tile_valid[c];
-        const int lim = min(kv_valid, c == g ? qi + 1 : kTile);  // keys < lim survive
+    // two register stages: the tile after next is loaded while this one is computed and the next
+    // one is waiting to go to LDS
+    uint4 stA[PER], stB[PER];
+    const int nt = g - first + 1;
+    // scaled, masked scores of key half kh of tile c (keys < lim survive)
+    auto tile_scores = [&](int buf, int c, int kh) {
+        f32x16 sc = scores<D>(qf, Kt[buf], kh, l32, hi);
+        const int lim = min(pv.tile_valid[c], c == g ? qi + 1 : kTile);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int key = 32 * kh + 8 * (i >> 2) + 4 * hi + (i & 3);
-            s[i] = key < lim ? s[i] * scale_log2 : -INFINITY;
+            sc[i] = key < lim ? sc[i] * scale_log2 : -INFINITY;
+        }
+        return sc;
+    };
+    // one pass over tiles first .. g: compute(e, buf) sees tile first + e in Kt[buf]
+    auto pass = [&](auto &&compute) {
+        stage_k_tile<D, NT>(stA, k, first, Hkv, kvh, tid);
+        store_k_tile<D, NT>(stA, Kt[0], tid);
+        if (nt > 1) stage_k_tile<D, NT>(stB, k, first + 1, Hkv, kvh, tid);
+        __syncthreads();
+        for (int e = 0; e < nt; e += 2) {
+            if (e + 2 < nt) stage_k_tile<D, NT>(stA, k, first + e + 2, Hkv, kvh, tid);
+            compute(e, 0);
+            if (e + 1 < nt) store_k_tile<D, NT>(stB, Kt[1], tid);
+            __syncthreads();
+            if (e + 1 >= nt) break;
+            if (e + 3 < nt) stage_k_tile<D, NT>(stB, k, first + e + 3, Hkv, kvh, tid);
+            compute(e + 1, 1);
+            if (e + 2 < nt) store_k_tile<D, NT>(stA, Kt[0], tid);
+            __syncthreads();
         }
     };
-    // pass 1: running max and sum of exp2 of every query over its causal keys
+    // pass 1: running max and sum of exp2 of this lane's query over its keys
     float m = -INFINITY, l = 0.0f;
-    for (int c = first; c <= g; ++c) {
-        __syncthreads();
-        load_k_rows<D>(Kt, k, static_cast<int64_t>(c) * kTile, Hkv, kvh, tid);
-        __syncthreads();
-        f32x16 s = scores<D>(qf, Kt, kh, l32, hi);
-        masked(s, c);
-        float mt = -INFINITY;
+    pass([&](int e, int buf) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[i]);
-        const float mn = fmaxf(m, mt);
-        if (mn > -INFINITY) {
-            float add = 0.0f;
+        for (int kh = 0; kh < 2; ++kh) {
+            const f32x16 sc = tile_scores(buf, first + e, kh);
+            float mt = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) add += exp2f(s[i] - mn);
-            l = l * exp2f(m - mn) + add;
-            m = mn;
+            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sc[i]);
+            const float mn = fmaxf(m, mt);
+            if (mn > -INFINITY) {
+                float add = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) add += __builtin_amdgcn_exp2f(sc[i] - mn);
+                l = l * __builtin_amdgcn_exp2f(m - mn) + add;
+                m = mn;
+            }
         }
-    }
-    // merge lanes l and l ^ 32 (same query, other keys), then the two key-half waves
-    {
+    });
+    {   // lanes l and l ^ 32 hold the same query's two key subsets
         const float m2 = __shfl_xor(m, 32, 64), l2 = __shfl_xor(l, 32, 64);
         const float mn = fmaxf(m, m2);
-        l = (mn == -INFINITY) ? 0.0f : l * exp2f(m - mn) + l2 * exp2f(m2 - mn);
-        m = mn;
-    }
-    if (hi == 0) {
-        ml[qh][kh][l32][0] = m;
-        ml[qh][kh][l32][1] = l;
-    }
-    __syncthreads();
-    {
-        const float m0 = ml[qh][0][l32][0], l0 = ml[qh][0][l32][1];
-        const float m1 = ml[qh][1][l32][0], l1 = ml[qh][1][l32][1];
-        const float mn = fmaxf(m0, m1);
-        l = (mn == -INFINITY) ? 0.0f : l0 * exp2f(m0 - mn) + l1 * exp2f(m1 - mn);
+        l = (mn == -INFINITY) ? 0.0f : l * __builtin_amdgcn_exp2f(m - mn) + l2 * __builtin_amdgcn_exp2f(m2 - mn);
         m = mn;
     }
     const float inv = (qi < q_valid && l > 0.0f) ? 1.0f / l : 0.0f;  // padded queries carry no mass
-    // pass 2: every key tile's mass
-    float *row = masses + (static_cast<int64_t>(h) * G + g) * RT;
-    for (int c = first; c <= g; ++c) {
-        __syncthreads();
-        load_k_rows<D>(Kt, k, static_cast<int64_t>(c) * kTile, Hkv, kvh, tid);
-        __syncthreads();
-        f32x16 s = scores<D>(qf, Kt, kh, l32, hi);
-        masked(s, c);
+    // pass 2: every key tile's mass; the two waves of a head are summed (in order) by one thread
+    // at the next step, after the barrier
+    float *row = masses + (static_cast<int64_t>(h - (wave >> 1)) * G + g) * RT;  // the group's first head
+    auto write_tile = [&](int e) {
+        if (tid < HPW) {
+            const float *pp = part[e & 1];
+            row[static_cast<int64_t>(tid) * G * RT + e] = pp[2 * tid] + pp[2 * tid + 1];
+        }
+    };
+    pass([&](int e, int buf) {
+        if (e > 0) write_tile(e - 1);
         float acc = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc += (s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m);
+        for (int kh = 0; kh < 2; ++kh) {
+            const f32x16 sc = tile_scores(buf, first + e, kh);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc += (sc[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - m);
+        }
         acc = wave_sum(acc * inv);
-        if (lane == 0) part[wave] = acc;
-        __syncthreads();
-        if (tid == 0) row[c - first] = (part[0] + part[1]) + (part[2] + part[3]);
-    }
+        if (lane == 0) part[e & 1][wave] = acc;
+    });
+    write_tile(nt - 1);  // after the last step's barrier
+}
+
+// GQA groups of 2 or 4 q heads per KV head: 4 or 8 wavefronts; four waves per SIMD (the kernel is
+// bound by latency: the resident waves hide each other's loads and barriers)
+template <int D, int HPW>
+__global__ __launch_bounds__(128 * HPW) __attribute__((amdgpu_waves_per_eu(2, 4))) void tile_mass_kernel(
+    PlanView pv, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, int Hq, int Hkv, float scale_log2,
+    float *__restrict__ masses, int RT) {
+    tile_mass_body<D, HPW>(pv, q, k, Hq, Hkv, scale_log2, masses, RT);
+}
+
+// one q head per workgroup (odd groups): two wavefronts stage a whole tile each, so more registers
+template <int D>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 2))) void tile_mass_kernel_one(
+    PlanView pv, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, int Hq, int Hkv, float scale_log2,
+    float *__restrict__ masses, int RT) {
+    tile_mass_body<D, 1>(pv, q, k, Hq, Hkv, scale_log2, masses, RT);
 }
 
 // One wavefront: sort 64 (mass, index) pairs by decreasing mass, ties by increasing index.
@@ -258,12 +312,22 @@ __global__ __launch_bounds__(64) void select_bits_kernel(PlanView pv, const floa
 hipError_t launch_tile_masses(const HostLayout &hl, const PlanView &pv, const uint16_t *q, const uint16_t *k,
                               float scale, float *masses, int RT, hipStream_t stream) {
     if (hl.G == 0) return hipSuccess;
-    const unsigned grid = static_cast<unsigned>(int64_t(hl.Hq) * hl.G);
+    const int group = hl.Hq / hl.Hkv;
+    const int hpw = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+    const unsigned grid = static_cast<unsigned>(int64_t(hl.Hkv) * (group / hpw) * hl.G);
     const float sl = scale * 1.4426950408889634f;
-    if (hl.D == 128)
-        tile_mass_kernel<128><<<grid, kEncThreads, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT);
-    else
-        tile_mass_kernel<64><<<grid, kEncThreads, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT);
+#define SIFT_TILE_MASS(DD, HH) \
+    tile_mass_kernel<DD, HH><<<grid, 128 * HH, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT)
+    if (hl.D == 128) {
+        if (hpw == 4) SIFT_TILE_MASS(128, 4);
+        else if (hpw == 2) SIFT_TILE_MASS(128, 2);
+        else tile_mass_kernel_one<128><<<grid, 128, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT);
+    } else {
+        if (hpw == 4) SIFT_TILE_MASS(64, 4);
+        else if (hpw == 2) SIFT_TILE_MASS(64, 2);
+        else tile_mass_kernel_one<64><<<grid, 128, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT);
+    }
+#undef SIFT_TILE_MASS
     return hipGetLastError();
 }
 

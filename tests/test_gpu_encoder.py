@@ -76,6 +76,22 @@ def test_masses_and_bits_small(seed, d):
         np.testing.assert_array_equal(ca, want_ca)
 
 
+@pytest.mark.parametrize("seed,hq,hkv,d", [(10, 3, 1, 128), (11, 2, 2, 64), (12, 8, 1, 64), (13, 4, 1, 128),
+                                          (14, 1, 1, 128), (15, 16, 2, 64)])
+def test_masses_gqa_groupings(seed, hq, hkv, d):
+    """Workgroups take 1, 2 or 4 q heads of a KV head (and several groups when the GQA group is
+    larger than 4): every grouping gives the oracle's masses."""
+    case = _small(seed, d, hq=hq, hkv=hkv)
+    print(f"encoder groups seed={seed} hq={hq} hkv={hkv} d={d}", flush=True)
+    lay, plan, m = _gpu_masses(case)
+    got = _full(case, m.cpu().numpy())
+    want = E.tile_masses(case)
+    tile_req, _, _, req_first, _, _ = E._segments(case)
+    for g in range(len(tile_req)):
+        t0 = int(req_first[tile_req[g]])
+        np.testing.assert_allclose(got[:, g, t0:g + 1], want[:, g, t0:g + 1], rtol=RTOL, atol=ATOL)
+
+
 def _long_doc_case(doc_tiles, seed=5):
     """One request, documents of the given tile counts (the last one ragged), a short question."""
     lens = [64 * t for t in doc_tiles]
