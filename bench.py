@@ -403,7 +403,7 @@ def main(argv=None):
             "ms_total": round(ms_pipe, 4),
             "ms_per_layer": round(ms_pipe / L, 5),
             "vs_single_layer_step": round(ms_pipe / L / ms_per_step, 3),
-            "note": "per-layer bits differ (same densities), H2D from pinned host one layer ahead; Q/K/V shared",
+            "note": "per-layer bits differ (same densities), H2D from pinned host two layers ahead, decode(l + 1) on its own stream beside attention(l); Q/K/V shared",
         }
     if not args.no_encoder:
         # the offline encoder on the same layer: per-tile softmax mass of the dense causal

@@ -5,16 +5,19 @@ vectors are computed offline per document, per layer and per head, kept in CPU D
 to the GPU at prefill time, where each layer decodes its bits and runs the sparse attention.
 
 This module is host orchestration only (streams, events, pinned buffers); every step of the
-path runs in the library's kernels.  Per layer l:
+path runs in the library's kernels.  Per layer l, on three streams (all at the default priority):
 
-  copy stream:    H2D of layer l's LA/CA words (pinned host -> one of two device slots)
-  compute stream: wait for that copy; sift_decode_bits -> CSR; sift_sparse_prefill -> O_l
+  copy stream:    H2D of layer l's LA/CA words (pinned host -> bit slot l % 2)
+  decode stream:  wait for that copy; sift_decode_bits -> CSR slot l % 2
+  compute stream: wait for that decode; sift_sparse_prefill -> O_l
 
-The copy of layer l + 1 is issued before layer l's kernels are enqueued, so it runs under layer
-l's attention.  The device bit slots are double buffered: layer l + 2's copy waits until layer l's
-decode, the last reader of that slot, has run.  The plan is uploaded once (it depends on the
-layout only) and the CSR and workspace buffers are reused by every layer (their users are all on
-the compute stream, so they are ordered).
+Layer l + 1's decode is enqueued right after layer l's attention, and layer l + 2's copy after
+that, so both run while layer l's attention does.  The attention kernel holds every CU while its
+queues last, and the decode kernels take the CUs its workgroups leave when they run dry.  The
+bit and CSR slots are double buffered.  Layer l + 2's copy waits until decode(l), the last reader
+of its bit slot, has run.  Decode(l + 2) waits until prefill(l), the last reader of its CSR slot,
+has run.  The decode stream has a workspace of its own, since the prefill's workspace is in use
+meanwhile.  The plan is uploaded once: it depends on the layout only.
 """
 from __future__ import annotations
 
@@ -58,47 +61,74 @@ class LayerPipeline:
         self.la_dev = [torch.empty(la_n, dtype=torch.int32, device=self.device) for _ in range(2)]
         self.ca_dev = [torch.empty(ca_n, dtype=torch.int32, device=self.device) for _ in range(2)]
         self.plan = B.plan_upload(layout, self.device)
-        self.row_ptr = torch.empty(layout.num_rows + 1, dtype=torch.int32, device=self.device)
-        self.col_idx = torch.empty(max(layout.csr_max_nnz, 1), dtype=torch.int32, device=self.device)
+        self.row_ptr = [torch.empty(layout.num_rows + 1, dtype=torch.int32, device=self.device) for _ in range(2)]
+        self.col_idx = [torch.empty(max(layout.csr_max_nnz, 1), dtype=torch.int32, device=self.device)
+                        for _ in range(2)]
         self.workspace = torch.empty(max(layout.workspace_bytes(dtype), layout.workspace_bytes(B.SIFT_BF16), 1),
                                      dtype=torch.uint8, device=self.device)
-        self.copy_stream = torch.cuda.Stream(device=self.device)  # default priority
+        self.decode_workspace = torch.empty(max(layout.workspace_bytes(B.SIFT_BF16), 1), dtype=torch.uint8,
+                                            device=self.device)
+        self.copy_stream = torch.cuda.Stream(device=self.device)    # default priority
+        self.decode_stream = torch.cuda.Stream(device=self.device)  # default priority
 
     def run(self, q_per_layer: Sequence, k_per_layer: Sequence, v_per_layer: Sequence,
             out_per_layer: Optional[List] = None, lse_per_layer: Optional[List] = None):
-        """Enqueue every layer on the current stream (the copies on the side stream); returns the
-        per-layer outputs.  Nothing here synchronises the device."""
+        """Enqueue every layer: the attention on the current stream, the copies and decodes on the
+        side streams; returns the per-layer outputs.  Nothing here synchronises the device."""
         torch = self.torch
         L = self.num_layers
         if not (len(q_per_layer) == len(k_per_layer) == len(v_per_layer) == L):
             raise ValueError("one Q, K and V per layer")
         compute = torch.cuda.current_stream(self.device)
         copied = [torch.cuda.Event() for _ in range(L)]
-        slot_free = [torch.cuda.Event() for _ in range(L)]
+        decoded = [torch.cuda.Event() for _ in range(L)]    # CSR slot l % 2 holds layer l; bit slot free
+        attended = [torch.cuda.Event() for _ in range(L)]   # prefill(l) done with CSR slot l % 2
         outs = out_per_layer if out_per_layer is not None else [None] * L
         lses = lse_per_layer if lse_per_layer is not None else [None] * L
+        # the caller's inputs (produced on the compute stream) and the plan must be ready before
+        # the side streams start
+        start = torch.cuda.Event()
+        start.record(compute)
 
         def issue_copy(l):
             s = l % 2
             with torch.cuda.stream(self.copy_stream):
+                self.copy_stream.wait_event(start)
                 if l >= 2:
-                    self.copy_stream.wait_event(slot_free[l - 2])
+                    self.copy_stream.wait_event(decoded[l - 2])
                 self.la_dev[s].copy_(self.la_host[l], non_blocking=True)
                 self.ca_dev[s].copy_(self.ca_host[l], non_blocking=True)
                 copied[l].record(self.copy_stream)
 
-        issue_copy(0)
-        for l in range(L):
-            if l + 1 < L:
-                issue_copy(l + 1)
+        def issue_decode(l):
             s = l % 2
-            compute.wait_event(copied[l])
-            B.decode_bits(self.layout, self.la_dev[s], self.ca_dev[s], plan=self.plan,
-                          workspace=self.workspace, row_ptr=self.row_ptr, col_idx=self.col_idx)
-            slot_free[l].record(compute)
+            with torch.cuda.stream(self.decode_stream):
+                self.decode_stream.wait_event(start)
+                self.decode_stream.wait_event(copied[l])
+                if l >= 2:
+                    self.decode_stream.wait_event(attended[l - 2])
+                B.decode_bits(self.layout, self.la_dev[s], self.ca_dev[s], plan=self.plan,
+                              workspace=self.decode_workspace, row_ptr=self.row_ptr[s], col_idx=self.col_idx[s])
+                decoded[l].record(self.decode_stream)
+
+        issue_copy(0)
+        issue_decode(0)
+        if L > 1:
+            issue_copy(1)
+        for l in range(L):
+            s = l % 2
+            compute.wait_event(decoded[l])
             o, lse = B.sparse_prefill(self.layout, q_per_layer[l], k_per_layer[l], v_per_layer[l],
-                                      self.row_ptr, self.col_idx, plan=self.plan, workspace=self.workspace,
+                                      self.row_ptr[s], self.col_idx[s], plan=self.plan, workspace=self.workspace,
                                       out=outs[l], lse=lses[l], want_lse=lses[l] is not None)
+            attended[l].record(compute)
             outs[l] = o
             lses[l] = lse
+            if l + 1 < L:
+                issue_decode(l + 1)
+            if l + 2 < L:
+                issue_copy(l + 2)
+        # the caller's stream is the last to touch every buffer: later work on it (or a reuse of
+        # this pipeline) is ordered after the side streams
+        compute.wait_event(decoded[L - 1])
         return outs, lses
