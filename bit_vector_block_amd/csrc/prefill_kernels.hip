@@ -120,7 +120,7 @@ __device__ inline LoadOffsets<D> make_load_offsets(int Hkv, int64_t N, int wave,
     using C = Cfg<D>;
     LoadOffsets<D> o;
     const uint32_t krow_bytes = static_cast<uint32_t>(Hkv) * D * 2;
-    const uint32_t vrow_bytes = static_cast<uint32_t>(N) * 2;
+    constexpr uint32_t vrow_bytes = kTile * 2;  // V^T rows of one tile are contiguous
 #pragma unroll
     for (int j = 0; j < C::KLOADS_W; ++j) {
         const int b = 1024 * (wave + kWaves * j) + 16 * lane;  // LDS byte this lane fills
@@ -197,7 +197,8 @@ __device__ __forceinline__ const uint16_t *k_tile_base(const RowCtx &c, int t) {
 }
 template <int D>
 __device__ __forceinline__ const uint16_t *vt_tile_base(const RowCtx &c, int t) {
-    return c.vt + static_cast<int64_t>(c.kvh) * D * c.N + static_cast<int64_t>(t < 0 ? 0 : t) * kTile;
+    // V^T is stored tile by tile: [Hkv][G][D][64], each tile one contiguous D x 128-byte block
+    return c.vt + (static_cast<int64_t>(c.kvh) * (c.N / kTile) + (t < 0 ? 0 : t)) * D * kTile;
 }
 
 // Operand reads of one step: K(e+1) rows for the scores, V^T(e) rows for the output.
@@ -897,8 +898,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-// V [N][Hkv][D] (bf16 or fp32, rounded to bf16) -> V^T [Hkv][D][N] with the tokens of every
-// 16-token group at vt_pos.  One workgroup per (64-token tile, kv head): the tile goes through
+// V [N][Hkv][D] (bf16 or fp32, rounded to bf16) -> V^T tiles [Hkv][G][D][64] (each 64-token tile's
+// D rows of 128 bytes contiguous, so that the attention's tile loads cover one 16 KB block) with
+// the tokens of every 16-token group at vt_pos.  One workgroup per (64-token tile, kv head): the tile goes through
 // LDS so that both the 2D-byte row reads and the 128-byte V^T row writes are whole rows.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const T *__restrict__ v, uint16_t *__restrict__ vt,
@@ -943,7 +945,7 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const T *__restrict__ 
         pk.y = w[2] | (uint32_t(w[3]) << 16);
         pk.z = w[4] | (uint32_t(w[5]) << 16);
         pk.w = w[6] | (uint32_t(w[7]) << 16);
-        *reinterpret_cast<uint4 *>(vt + (static_cast<int64_t>(kvh) * D + d) * N + tok0 + 8 * c) = pk;
+        *reinterpret_cast<uint4 *>(vt + ((static_cast<int64_t>(kvh) * (N / kTile) + t) * D + d) * kTile + 8 * c) = pk;
     }
 }
 

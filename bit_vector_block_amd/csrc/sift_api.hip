@@ -187,7 +187,7 @@ size_t decode_workspace_bytes(const HostLayout &hl) {
            align256(sizeof(int32_t) * size_t(hl.Hq));
 }
 
-// Prefill scratch: 256 bytes of row-queue counters, V^T (bf16 [Hkv][D][N]); for SIFT_FP32
+// Prefill scratch: 256 bytes of row-queue counters, V^T (bf16 tiles [Hkv][G][D][64]); for SIFT_FP32
 // inputs the bf16 copies of Q and K follow.  The fused path (no CSR) appends its pre-pass
 // tables: ca_prefix [Hq][ndocs], ca_list [Hq][G], rowinfo [Hq][G][8] (int32).
 constexpr size_t kCounterBytes = 256;

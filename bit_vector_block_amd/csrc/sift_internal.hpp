@@ -66,7 +66,7 @@ hipError_t launch_tile_masses(const HostLayout &hl, const PlanView &pv, const ui
 hipError_t launch_select_bits(const HostLayout &hl, const PlanView &pv, const float *masses, int RT, float p_la,
                               float p_ca, uint32_t *la_out, uint32_t *ca_out, hipStream_t stream);
 hipError_t launch_cast_bf16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);
-// V [N][Hkv][D] (bf16, or fp32 when fp32 is set) -> bf16 V^T [Hkv][D][N] in the prefill layout;
+// V [N][Hkv][D] (bf16, or fp32 when fp32 is set) -> bf16 V^T tiles [Hkv][G][D][64] in the prefill layout;
 // also zeroes the 8 row-queue counters the attention kernel claims rows from.
 hipError_t launch_transpose_v(const HostLayout &hl, const void *v, bool fp32, uint16_t *vt, int *counters,
                               hipStream_t stream);

@@ -148,8 +148,8 @@ sift_status sift_decode_bits(const sift_layout *layout, const void *d_plan,
  * [Hq][N] may be NULL.  Listed tiles outside [0, G) are skipped.
  * d_q, d_k, d_v, d_out and d_workspace must be 16-byte aligned (SIFT_ERR_INVALID otherwise).
  * d_workspace: >= sift_workspace_bytes(layout, dtype) bytes of scratch; it holds
- * V transposed to bf16 [Hkv][D][N] (written by the call, in a token order
- * internal to the library) and, for SIFT_FP32 inputs, the bf16 copies of Q and K.
+ * V transposed to bf16, tile by tile [Hkv][G][D][64] (written by the call, in a
+ * token order internal to the library) and, for SIFT_FP32 inputs, the bf16 copies of Q and K.
  * Errors: SIFT_ERR_INVALID, SIFT_ERR_CAPACITY (workspace),
  * SIFT_ERR_UNSUPPORTED (head_dim, tile), SIFT_ERR_HIP.
  */
