@@ -9,11 +9,14 @@
 //
 // Two launches, both stream-ordered, no host read-back:
 //   decode_count  (one workgroup per q head): per-document CA popcounts and
-//                 their per-request exclusive prefix, per-row counts in closed
-//                 form, a block scan over the head's G rows -> row offsets
-//                 relative to the head, and the head's total;
+//                 their per-request exclusive prefix (block scans), the
+//                 head's CA page list of every request (document order), the
+//                 per-row counts in closed form, block scans over the head's
+//                 G rows -> row offsets relative to the head, and the head's
+//                 total;
 //   decode_fill   (one wavefront per row): adds the totals of earlier heads,
-//                 writes row_ptr, and expands the row's candidate bits with
+//                 writes row_ptr, copies the row's CA part (a leading slice
+//                 of its request's page list) and expands its LA bits with
 //                 one lane per bit: ballot gives the set mask, mbcnt the
 //                 lane's rank among the set bits, so the 64 lanes write their
 //                 tile ids in order with no atomics.
@@ -55,58 +58,50 @@ __device__ inline int row_count(const PlanView &pv, const uint32_t *la, const in
     return ca_prefix_h[d] + popcount_range(vec, lo, lo + r);
 }
 
-__global__ __launch_bounds__(kCountThreads) void decode_count_kernel(
-    PlanView pv, const uint32_t *__restrict__ la, const uint32_t *__restrict__ ca,
-    int32_t *__restrict__ ca_prefix, int32_t *__restrict__ row_local,
-    int32_t *__restrict__ head_total) {
-    if (!plan_ok(pv)) return;
-    const int h = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int ndocs = pv.num_docs, G = pv.num_tiles;
-    int32_t *pref = ca_prefix + static_cast<int64_t>(h) * ndocs;
-
-    // 1. CA popcount of every (doc, h) vector (bits past T are ignored).
-    for (int d = tid; d < ndocs; d += kCountThreads) {
-        const uint32_t *vec = ca + pv.doc_ca_off[d] + h * pv.doc_ca_w[d];
-        pref[d] = popcount_range(vec, 0, pv.doc_tiles[d] - 1);
+// Exclusive scan of one int per thread over a workgroup of kCountThreads threads (wave scans, then
+// the wave totals through sh[kCountThreads / 64]); total gets the workgroup's sum.  Every thread
+// of the workgroup calls it.
+__device__ inline int block_excl_scan(int x, int *sh, int &total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int incl = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
     }
+    if (lane == 63) sh[wave] = incl;
     __syncthreads();
-    // 2. Exclusive prefix over the documents of each request (serial per request).
-    for (int b = tid; b < pv.num_requests; b += kCountThreads) {
-        int acc = 0;
-        const int d0 = pv.req_first_doc[b], d1 = d0 + pv.req_ndocs[b];
-        for (int d = d0; d < d1; ++d) {
-            const int c = pref[d];
-            pref[d] = acc;
-            acc += c;
-        }
+    int below = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kCountThreads / 64; ++w) {
+        const int v = sh[w];
+        below += w < wave ? v : 0;
+        all += v;
     }
-    __syncthreads();
-    // 3. Row counts: each thread owns a contiguous run of tiles; block scan of the run sums.
-    __shared__ int run_sum[kCountThreads];
-    const int per = (G + kCountThreads - 1) / kCountThreads;
-    const int g0 = min(G, tid * per), g1 = min(G, g0 + per);
-    int s = 0;
-    for (int g = g0; g < g1; ++g) s += row_count(pv, la, pref, h, g);
-    run_sum[tid] = s;
-    __syncthreads();
-    for (int off = 1; off < kCountThreads; off <<= 1) {
-        const int add = tid >= off ? run_sum[tid - off] : 0;
-        __syncthreads();
-        run_sum[tid] += add;
-        __syncthreads();
-    }
-    int base = run_sum[tid] - s;  // exclusive
-    int32_t *loc = row_local + static_cast<int64_t>(h) * G;
-    for (int g = g0; g < g1; ++g) {
-        loc[g] = base;
-        base += row_count(pv, la, pref, h, g);
-    }
-    if (tid == kCountThreads - 1) head_total[h] = run_sum[tid];
+    __syncthreads();  // sh is free again
+    total = all;
+    return below + incl - x;
 }
 
-__global__ void zero_kernel(int32_t *p, int n) {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+// pref[d] = CA entries of the earlier documents of d's request, for q head h: the CA popcounts of
+// all documents scanned in chunks of kCountThreads, then each document's value less that of its
+// request's first document.  tmp: >= ndocs ints of scratch in global memory.
+__device__ inline void head_ca_prefix(const PlanView &pv, const uint32_t *__restrict__ ca, int h, int32_t *pref,
+                                      int32_t *tmp, int *sh) {
+    const int tid = threadIdx.x, ndocs = pv.num_docs;
+    int carry = 0;
+    for (int base = 0; base < ndocs; base += kCountThreads) {
+        const int d = base + tid;
+        const int c = d < ndocs ? popcount_range(ca + pv.doc_ca_off[d] + h * pv.doc_ca_w[d], 0, pv.doc_tiles[d] - 1)
+                                : 0;
+        int total;
+        const int ex = block_excl_scan(c, sh, total);
+        if (d < ndocs) tmp[d] = carry + ex;  // CA entries of every earlier document of the batch
+        carry += total;
+    }
+    __syncthreads();
+    for (int d = tid; d < ndocs; d += kCountThreads) pref[d] = tmp[d] - tmp[pv.req_first_doc[pv.doc_req[d]]];
+    __syncthreads();
 }
 
 __device__ inline int lane_rank(uint64_t mask) {
@@ -115,14 +110,68 @@ __device__ inline int lane_rank(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
 }
 
+// lst[req_first[b] + k] = the k-th CA-marked page of request b for q head h, in document order (the
+// CA part of every document row of the request is a leading slice of it).  One thread per
+// document walks its set bits in order, so all documents proceed at once.  pref from
+// head_ca_prefix.
+__device__ inline void head_ca_list(const PlanView &pv, const uint32_t *__restrict__ ca, int h,
+                                    const int32_t *pref, int32_t *lst) {
+    for (int d = threadIdx.x; d < pv.num_docs; d += kCountThreads) {
+        const uint32_t *vec = ca + pv.doc_ca_off[d] + h * pv.doc_ca_w[d];
+        const int T = pv.doc_tiles[d], t0 = pv.doc_first[d];
+        int pos = pv.req_first[pv.doc_req[d]] + pref[d];
+        for (int w = 0; 32 * w < T; ++w) {
+            uint32_t bits = vec[w];
+            if (T - 32 * w < 32) bits &= (1u << (T - 32 * w)) - 1u;  // bits past T are ignored
+            while (bits != 0u) {
+                lst[pos++] = t0 + 32 * w + __builtin_ctz(bits);
+                bits &= bits - 1u;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kCountThreads) void decode_count_kernel(
+    PlanView pv, const uint32_t *__restrict__ la, const uint32_t *__restrict__ ca,
+    int32_t *__restrict__ ca_prefix, int32_t *__restrict__ ca_list, int32_t *__restrict__ row_local,
+    int32_t *__restrict__ head_total) {
+    if (!plan_ok(pv)) return;
+    const int h = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int ndocs = pv.num_docs, G = pv.num_tiles;
+    int32_t *pref = ca_prefix + static_cast<int64_t>(h) * ndocs;
+    int32_t *loc = row_local + static_cast<int64_t>(h) * G;
+    __shared__ int sh[kCountThreads / 64];
+    // 1. Per document: CA entries of the earlier documents of its request (bits past T ignored);
+    //    the head's row offsets (G >= ndocs entries) serve as the scratch.
+    head_ca_prefix(pv, ca, h, pref, loc, sh);
+    // 2. The head's CA page list per request (the fill copies each row's CA part from it).
+    head_ca_list(pv, ca, h, pref, ca_list + static_cast<int64_t>(h) * G);
+    // 3. Row counts in closed form, scanned kCountThreads rows at a time -> offsets in the head.
+    int carry = 0;
+    for (int base = 0; base < G; base += kCountThreads) {
+        const int g = base + tid;
+        const int c = g < G ? row_count(pv, la, pref, h, g) : 0;
+        int total;
+        const int ex = block_excl_scan(c, sh, total);
+        if (g < G) loc[g] = carry + ex;
+        carry += total;
+    }
+    if (tid == 0) head_total[h] = carry;
+}
+
+__global__ void zero_kernel(int32_t *p, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
 __device__ inline int wave_sum(int x) {
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
     return x;
 }
 
 __global__ __launch_bounds__(64 * kFillWaves) void decode_fill_kernel(
-    PlanView pv, const uint32_t *__restrict__ la, const uint32_t *__restrict__ ca,
-    const int32_t *__restrict__ ca_prefix, const int32_t *__restrict__ row_local,
+    PlanView pv, const uint32_t *__restrict__ la, const int32_t *__restrict__ ca_prefix,
+    const int32_t *__restrict__ ca_list, const int32_t *__restrict__ row_local,
     const int32_t *__restrict__ head_total, int32_t *__restrict__ row_ptr,
     int32_t *__restrict__ col_idx) {
     if (!plan_ok(pv)) return;
@@ -151,20 +200,12 @@ __global__ __launch_bounds__(64 * kFillWaves) void decode_fill_kernel(
         for (int c = lane; c < cnt; c += 64) col_idx[start + c] = first + c;
         return;
     }
-    int pos = start;
-    // CA pages of the earlier documents of the same request
-    const int first_doc = pv.req_first_doc[pv.doc_req[d]];
-    for (int i = first_doc; i < d; ++i) {
-        const uint32_t *vec = ca + pv.doc_ca_off[i] + h * pv.doc_ca_w[i];
-        const int T = pv.doc_tiles[i], t0 = pv.doc_first[i];
-        for (int c0 = 0; c0 < T; c0 += 64) {
-            const int c = c0 + lane;
-            const bool bit = c < T && ((vec[c >> 5] >> (c & 31)) & 1u);
-            const uint64_t mask = __ballot(bit);
-            if (bit) col_idx[pos + lane_rank(mask)] = t0 + c;
-            pos += __popcll(mask);
-        }
-    }
+    // CA pages of the earlier documents of the same request: the leading slice of the request's
+    // CA page list
+    const int nca = ca_prefix[static_cast<int64_t>(h) * pv.num_docs + d];
+    const int32_t *src = ca_list + static_cast<int64_t>(h) * G + pv.req_first[pv.doc_req[d]];
+    for (int c = lane; c < nca; c += 64) col_idx[start + c] = src[c];
+    int pos = start + nca;
     // LA tiles c <= r of the row's own document
     const int r = pv.tile_local[g];
     const uint32_t *vec = la + pv.doc_la_off[d] + h * pv.doc_la_w[d];
@@ -193,35 +234,10 @@ __global__ __launch_bounds__(kCountThreads) void bits_prepass_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ndocs = pv.num_docs, G = pv.num_tiles;
     int32_t *pref = ca_prefix + static_cast<int64_t>(h) * ndocs;
-    for (int d = tid; d < ndocs; d += kCountThreads) {
-        const uint32_t *vec = ca + pv.doc_ca_off[d] + h * pv.doc_ca_w[d];
-        pref[d] = popcount_range(vec, 0, pv.doc_tiles[d] - 1);
-    }
-    __syncthreads();
-    for (int b = tid; b < pv.num_requests; b += kCountThreads) {
-        int acc = 0;
-        const int d0 = pv.req_first_doc[b], d1 = d0 + pv.req_ndocs[b];
-        for (int d = d0; d < d1; ++d) {
-            const int c = pref[d];
-            pref[d] = acc;
-            acc += c;
-        }
-    }
-    __syncthreads();
-    // CA pages of each document, one wavefront per document: ballot and lane rank place them
     int32_t *lst = ca_list + static_cast<int64_t>(h) * G;
-    for (int d = wave; d < ndocs; d += kCountThreads / 64) {
-        const uint32_t *vec = ca + pv.doc_ca_off[d] + h * pv.doc_ca_w[d];
-        const int T = pv.doc_tiles[d], t0 = pv.doc_first[d];
-        int pos = pv.req_first[pv.doc_req[d]] + pref[d];
-        for (int c0 = 0; c0 < T; c0 += 64) {
-            const int c = c0 + lane;
-            const bool bit = c < T && ((vec[c >> 5] >> (c & 31)) & 1u);
-            const uint64_t mask = __ballot(bit);
-            if (bit) lst[pos + lane_rank(mask)] = t0 + c;
-            pos += __popcll(mask);
-        }
-    }
+    __shared__ int sh[kCountThreads / 64];
+    head_ca_prefix(pv, ca, h, pref, lst, sh);  // the head's page list (G >= ndocs) as scratch
+    head_ca_list(pv, ca, h, pref, lst);
     // per-row records
     for (int g = tid; g < G; g += kCountThreads) {
         int32_t *ri = rowinfo + (static_cast<int64_t>(h) * G + g) * 8;
@@ -270,18 +286,19 @@ hipError_t launch_decode(const HostLayout &hl, const PlanView &pv, const uint32_
     int32_t *ca_prefix = reinterpret_cast<int32_t *>(ws);
     int32_t *row_local = reinterpret_cast<int32_t *>(ws + a0);
     int32_t *head_total = reinterpret_cast<int32_t *>(ws + a0 + a1);
+    int32_t *ca_list = reinterpret_cast<int32_t *>(ws + a0 + a1 + ((sizeof(int32_t) * size_t(hl.Hq) + 255) & ~size_t(255)));
     if (hl.G == 0) {  // no rows: row_ptr[0] = 0
         zero_kernel<<<1, 64, 0, stream>>>(row_ptr, 1);
         return hipGetLastError();
     }
-    decode_count_kernel<<<hl.Hq, kCountThreads, 0, stream>>>(pv, la, ca, ca_prefix, row_local,
+    decode_count_kernel<<<hl.Hq, kCountThreads, 0, stream>>>(pv, la, ca, ca_prefix, ca_list, row_local,
                                                               head_total);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nrows = int64_t(hl.Hq) * hl.G;
     const int64_t blocks = (nrows + kFillWaves - 1) / kFillWaves;
     decode_fill_kernel<<<static_cast<unsigned>(blocks), 64 * kFillWaves, 0, stream>>>(
-        pv, la, ca, ca_prefix, row_local, head_total, row_ptr, col_idx);
+        pv, la, ca_prefix, ca_list, row_local, head_total, row_ptr, col_idx);
     return hipGetLastError();
 }
 

@@ -181,10 +181,13 @@ PlanView plan_view(const HostLayout &hl, const void *d_plan) {
 }
 
 // Decode scratch: ca_prefix [Hq][ndocs], row_local [Hq][G], head_total [Hq].
+// Decode scratch: ca_prefix [Hq][ndocs], row offsets [Hq][G], head totals [Hq], CA page lists
+// [Hq][G] (int32).
 size_t decode_workspace_bytes(const HostLayout &hl) {
     return align256(sizeof(int32_t) * size_t(hl.Hq) * size_t(std::max(hl.ndocs, 1))) +
            align256(sizeof(int32_t) * size_t(hl.Hq) * size_t(std::max(hl.G, 1))) +
-           align256(sizeof(int32_t) * size_t(hl.Hq));
+           align256(sizeof(int32_t) * size_t(hl.Hq)) +
+           align256(sizeof(int32_t) * size_t(hl.Hq) * size_t(std::max(hl.G, 1)));
 }
 
 // Prefill scratch: 256 bytes of row-queue counters, V^T (bf16 tiles [Hkv][G][D][64]); for SIFT_FP32
