@@ -144,3 +144,25 @@ def test_encoder_config2_sampled_rows_and_all_bits():
     la, ca = _gpu_select(lay, plan, m, 0.9, 0.9)
     np.testing.assert_array_equal(la, want_la)
     np.testing.assert_array_equal(ca, want_ca)
+
+
+def test_encoder_config4_sampled_rows_and_all_bits():
+    """The Qwen3-235B shape (64 q heads, 4 KV heads: four groups of four q heads per KV head,
+    20 documents of 2048 tokens): masses on sampled rows, every head's bits."""
+    case = config(4)
+    print("encoder config 4", flush=True)
+    lay, plan, m = _gpu_masses(case)
+    got = _full(case, m.cpu().numpy())
+    rng = np.random.default_rng(4044)
+    G = lay.num_tiles
+    samples = [(0, 0), (63, G - 1), (17, 40), (46, 333)] + [
+        (int(rng.integers(0, 64)), int(rng.integers(0, G))) for _ in range(4)]
+    for h, g in samples:
+        want = E.tile_mass_row(case, h, g)
+        np.testing.assert_allclose(got[h, g, : g + 1], want[: g + 1], rtol=RTOL, atol=ATOL,
+                                   err_msg=f"row h={h} g={g}")
+    la_b, ca_b = E.select_bits(case, got, 0.9, 0.9)
+    want_la, want_ca = W.pack_bits(la_b, ca_b)
+    la, ca = _gpu_select(lay, plan, m, 0.9, 0.9)
+    np.testing.assert_array_equal(la, want_la)
+    np.testing.assert_array_equal(ca, want_ca)
