@@ -16,9 +16,9 @@
 //                    two passes over the row's causal key tiles: the row max and sum of every
 //                    query, then every tile's mass (bf16 MFMA scores, fp32 softmax,
 //                    deterministic reductions); each K tile is loaded once for the group;
-// select_bits_kernel one wavefront per (q head, document): bitonic sort of the candidates, an
-//                    inclusive Hillis-Steele scan (the order in which the threshold test sums),
-//                    the cut, and the bit packing in LDS.
+// select_bits_kernel one workgroup per (q head, document), a wavefront per LA row: bitonic sort
+//                    of the candidates, an inclusive Hillis-Steele scan (the order in which the
+//                    threshold test sums), the cut, and the bit packing in LDS.
 #include <math.h>
 
 #include "sift_internal.hpp"
@@ -264,47 +264,62 @@ __device__ inline bool top_p_keep(float mass, int n, float p, int lane) {
     return mine;
 }
 
-__global__ __launch_bounds__(64) void select_bits_kernel(PlanView pv, const float *__restrict__ masses, int RT,
-                                                         float p_la, float p_ca, uint32_t *__restrict__ la_out,
-                                                         uint32_t *__restrict__ ca_out) {
-    __shared__ uint32_t words[72];
+constexpr int kSelectWaves = 4;
+
+// One workgroup of kSelectWaves wavefronts per (q head, document): the LA rows are spread over
+// the wavefronts (each row's top-p cut is a one-wavefront operation), then wavefront 0 selects the
+// CA pages.  The bits are packed in LDS and written out whole.
+__global__ __launch_bounds__(64 * kSelectWaves) void select_bits_kernel(PlanView pv, const float *__restrict__ masses,
+                                                                        int RT, float p_la, float p_ca,
+                                                                        uint32_t *__restrict__ la_out,
+                                                                        uint32_t *__restrict__ ca_out) {
+    __shared__ uint32_t la_words[72];  // T <= 64: at most 65 words
+    __shared__ uint32_t ca_words[4];
     if (!plan_ok(pv)) return;
     const int G = pv.num_tiles;
-    const int h = blockIdx.x, d = blockIdx.y, lane = threadIdx.x;
+    const int h = blockIdx.x, d = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = pv.doc_tiles[d], t0 = pv.doc_first[d], b = pv.doc_req[d];
     const int first = pv.req_first[b];
     const int dl = pv.req_first_doc[b] + pv.req_ndocs[b] - 1;
     const int doc_end = pv.doc_first[dl] + pv.doc_tiles[dl];  // the request's question starts here
-    // LA: one triangle row at a time
-    const int law = pv.doc_la_w[d];
-    for (int w = lane; w < law; w += 64) words[w] = 0u;
+    const int law = pv.doc_la_w[d], caw = pv.doc_ca_w[d];
+    for (int w = tid; w < law; w += 64 * kSelectWaves) la_words[w] = 0u;
+    for (int w = tid; w < caw; w += 64 * kSelectWaves) ca_words[w] = 0u;
     __syncthreads();
-    for (int r = 0; r < T; ++r) {
+    // LA: triangle rows r = wave, wave + kSelectWaves, ...
+    for (int r = wave; r < T; r += kSelectWaves) {
         const int gq = t0 + r;
         const float mass = lane <= r ? masses[(static_cast<int64_t>(h) * G + gq) * RT + (t0 + lane - first)] : 0.0f;
         const bool keep = top_p_keep(mass, r + 1, p_la, lane) || lane == r || lane == 0;
         if (lane <= r && keep) {
             const int bit = r * (r + 1) / 2 + lane;
-            atomicOr(&words[bit >> 5], 1u << (bit & 31));
+            atomicOr(&la_words[bit >> 5], 1u << (bit & 31));
         }
+    }
+    // CA: page masses from the later documents' query tiles, summed in increasing tile order (the
+    // loads go out eight at a time, the additions stay in order)
+    if (wave == 0) {
+        float cm = 0.0f;
+        if (lane < T) {
+            const float *col = masses + static_cast<int64_t>(h) * G * RT + (t0 + lane - first);
+            int gq = t0 + T;
+            for (; gq + 8 <= doc_end; gq += 8) {
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = col[static_cast<int64_t>(gq + j) * RT];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) cm += v[j];
+            }
+            for (; gq < doc_end; ++gq) cm += col[static_cast<int64_t>(gq) * RT];
+        }
+        const bool keep = top_p_keep(cm, T, p_ca, lane) || lane == 0;
+        if (lane < T && keep) atomicOr(&ca_words[lane >> 5], 1u << (lane & 31));
     }
     __syncthreads();
     uint32_t *la_vec = la_out + pv.doc_la_off[d] + h * law;
-    for (int w = lane; w < law; w += 64) la_vec[w] = words[w];
-    __syncthreads();
-    // CA: page masses from the later documents' query tiles
-    const int caw = pv.doc_ca_w[d];
-    for (int w = lane; w < caw; w += 64) words[w] = 0u;
-    __syncthreads();
-    float cm = 0.0f;
-    if (lane < T)
-        for (int gq = t0 + T; gq < doc_end; ++gq)
-            cm += masses[(static_cast<int64_t>(h) * G + gq) * RT + (t0 + lane - first)];
-    const bool keep = top_p_keep(cm, T, p_ca, lane) || lane == 0;
-    if (lane < T && keep) atomicOr(&words[lane >> 5], 1u << (lane & 31));
-    __syncthreads();
+    for (int w = tid; w < law; w += 64 * kSelectWaves) la_vec[w] = la_words[w];
     uint32_t *ca_vec = ca_out + pv.doc_ca_off[d] + h * caw;
-    for (int w = lane; w < caw; w += 64) ca_vec[w] = words[w];
+    for (int w = tid; w < caw; w += 64 * kSelectWaves) ca_vec[w] = ca_words[w];
 }
 
 }  // namespace
@@ -335,7 +350,7 @@ hipError_t launch_select_bits(const HostLayout &hl, const PlanView &pv, const fl
                               float p_ca, uint32_t *la_out, uint32_t *ca_out, hipStream_t stream) {
     if (hl.ndocs == 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(hl.Hq), static_cast<unsigned>(hl.ndocs));
-    select_bits_kernel<<<grid, 64, 0, stream>>>(pv, masses, RT, p_la, p_ca, la_out, ca_out);
+    select_bits_kernel<<<grid, 64 * kSelectWaves, 0, stream>>>(pv, masses, RT, p_la, p_ca, la_out, ca_out);
     return hipGetLastError();
 }
 
