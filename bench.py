@@ -202,8 +202,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sharding is by q-head groups or by request, see the design notes); run with --gpus 1",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (it would shard by "
+              "groups of q heads that share a KV head, or by request, with no exchange); run with --gpus 1",
               file=sys.stderr)
         return 2
 

@@ -5,7 +5,7 @@ each retrieved document is prefilled densely once; the positions with high atten
 are recorded as two bit vectors per document, layer and head -- Local-Attention (LA) bits for
 the tiles of the document's own attention matrix, Cross-Attention (CA) bits for the document's
 KV pages that draw attention from other documents.  The pages do not state the selection rule;
-the reading used here (stated in the design notes) is:
+the reading used here is:
 
   * attention is the dense causal attention of the whole request (documents in order, then the
     question), scale 1/sqrt(D), GQA, padded tokens excluded;
