@@ -112,7 +112,7 @@ __device__ inline void wait_vmcnt_le(int n) {
 template <int D>
 struct LoadOffsets {
     uint32_t k[Cfg<D>::KLOADS_W];
-    uint32_t v[Cfg<D>::VLOADS_W];
+    uint32_t v[2];  // loads j and j + 2 of a V^T tile differ by 2048 bytes
 };
 
 template <int D>
@@ -127,8 +127,9 @@ __device__ inline LoadOffsets<D> make_load_offsets(int Hkv, int64_t N, int wave,
         const int r = b / C::KROW, c = (b % C::KROW) / 16;
         o.k[j] = r * krow_bytes + 16u * static_cast<uint32_t>(c < C::CPR ? c : 0);
     }
+    static_assert(C::VLOADS_W % 2 == 0, "V^T loads come in pairs");
 #pragma unroll
-    for (int j = 0; j < C::VLOADS_W; ++j) {
+    for (int j = 0; j < 2; ++j) {
         const int I = wave * C::VLOADS_W + j;  // this load fills V^T tile bytes [1024 I, 1024 I + 1024)
         const int d = I * 8 + lane / 8;
         o.v[j] = d * vrow_bytes + 16u * static_cast<uint32_t>(vt_slot(d, lane % 8));
@@ -136,28 +137,45 @@ __device__ inline LoadOffsets<D> make_load_offsets(int Hkv, int64_t N, int wave,
     return o;
 }
 
+// The tile loads are buffer loads into LDS: the tile's (uniform) base address sits in the buffer
+// descriptor (scalar registers), each lane supplies only its 32-bit offset, so no per-load vector
+// address arithmetic is needed.  Word 3 of the descriptor is the gfx9 raw-buffer default.
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot type-check these builtins
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+#endif
+
 // Direct-to-LDS load of one K tile (base = the tile's first token row of this kv head).
 template <int D>
 __device__ __forceinline__ void load_k_tile(const uint16_t *base, char *dst, int wave, const uint32_t *off) {
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot type-check this builtin
+#if defined(__HIP_DEVICE_COMPILE__)
     using C = Cfg<D>;
-    const char *g = reinterpret_cast<const char *>(base);  // uniform
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(base);  // uniform
 #pragma unroll
     for (int j = 0; j < C::KLOADS_W; ++j)
         if (wave + kWaves * j < C::KLOADS)
-            __builtin_amdgcn_global_load_lds(g + off[j], (lds_void *)(dst + 1024 * (wave + kWaves * j)), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + 1024 * (wave + kWaves * j)), 16,
+                                                     static_cast<int>(off[j]), 0, 0, 0);
 #endif
 }
 
 // Direct-to-LDS load of one V^T tile (base = row d = 0 of this kv head at the tile's first token).
+// Loads j and j + 2 cover rows 16 apart: same swizzle, 2048 bytes further on both sides, which is
+// the instruction's immediate offset (added to the global and to the LDS address alike).
 template <int D>
 __device__ __forceinline__ void load_vt_tile(const uint16_t *base, char *dst, int wave, const uint32_t *off) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = Cfg<D>;
-    const char *g = reinterpret_cast<const char *>(base);  // uniform
-#pragma unroll
-    for (int j = 0; j < C::VLOADS_W; ++j)
-        __builtin_amdgcn_global_load_lds(g + off[j], (lds_void *)(dst + 1024 * (wave * C::VLOADS_W + j)), 16, 0, 0);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(base);  // uniform
+    static_assert(C::VLOADS_W == 2 || C::VLOADS_W == 4, "two or four V^T loads per wave");
+    char *d0 = dst + 1024 * wave * C::VLOADS_W;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)d0, 16, static_cast<int>(off[0]), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(d0 + 1024), 16, static_cast<int>(off[1]), 0, 0, 0);
+    if constexpr (C::VLOADS_W == 4) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)d0, 16, static_cast<int>(off[0]), 0, 2048, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(d0 + 1024), 16, static_cast<int>(off[1]), 0, 2048, 0);
+    }
 #endif
 }
 
