@@ -189,3 +189,22 @@ def test_prefill_empty_rows():
     case = W.with_bits(case, la, ca)
     out, lse = gpu_prefill(case)
     assert np.all(out == 0.0) and np.all(np.isneginf(lse))
+
+
+def test_prefill_nan_in_padded_queries():
+    """NaN in the Q of padded query slots stays in those slots: a query's softmax state lives in
+    its own lanes, so every valid query's output and LSE are bit-identical to a run with finite
+    padding, and padded query rows are still exactly 0 with LSE -inf (question and documents
+    not tile-aligned, GQA)."""
+    case = W.make_case("pad-q", 810, [2], [150, 90], [40], 4, 2, 128,
+                       np.full((1, 4), 0.5), np.full((1, 4), 0.5))
+    out0, lse0 = gpu_prefill(case)
+    valid = valid_tokens(case)
+    assert (~valid).any()
+    q = case.q.copy()
+    q[~valid] = np.uint16(0x7FC0)  # bf16 quiet NaN
+    out1, lse1 = gpu_prefill(case, q=q)
+    assert np.array_equal(out1[valid], out0[valid])
+    assert np.array_equal(lse1[:, valid], lse0[:, valid])
+    assert np.all(out1[~valid] == 0.0)
+    assert np.all(np.isneginf(lse1[:, ~valid]))
