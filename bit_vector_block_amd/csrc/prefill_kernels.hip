@@ -14,8 +14,9 @@
 //    with the tokens of every 16-token group stored in the order the PV
 //    operands consume them, so that every MFMA operand -- K for the scores,
 //    V^T for the output -- is one 16-byte LDS read per lane;
-//  * K and V^T tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
-//    register staging), double buffered so the next listed tile streams in
+//  * K and V^T tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds:
+//    the tile's base address in a scalar buffer descriptor, a 32-bit offset per
+//    lane, no register staging), double buffered so the next listed tile streams in
 //    while the current one is multiplied.  K rows are padded by 16 bytes and
 //    V^T 16-byte chunks are XOR-swizzled per row, so the operand reads are free
 //    of bank conflicts and K's need a single address register;
