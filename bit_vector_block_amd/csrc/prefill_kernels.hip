@@ -240,16 +240,6 @@ __device__ __forceinline__ void read_vt(bf16x8 (&vf)[D / 16], const char *Vt, co
     }
 }
 
-template <int D>
-__device__ __forceinline__ void read_vt_half(bf16x8 (&vf)[D / 16], const char *Vt, const RowCtx &c, int half) {
-    const int hi = c.lane >> 5, kh = c.wave >> 1, l32 = c.lane & 31;
-#pragma unroll
-    for (int q = half * (D / 32); q < (half + 1) * (D / 32); ++q) {
-        const int d = 32 * (q >> 1) + l32, ch = 4 * kh + 2 * (q & 1) + hi;
-        vf[q] = *reinterpret_cast<const bf16x8 *>(Vt + d * 128 + 16 * vt_slot(d, ch));
-    }
-}
-
 __device__ __forceinline__ bool needs_mask(int t, int kv_valid, const RowCtx &c) {
     return kv_valid < kTile || t >= c.g;
 }
@@ -324,16 +314,34 @@ __device__ __forceinline__ void exp_pv_tile(WaveState<D> &st, const f32x16 &s, f
         st.acc_o[q >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[q], pb[q & 1], st.acc_o[q >> 1], 0, 0, 0);
 }
 
+// The V^T operands of one parity of PV K-steps, q = PAR, PAR + 2, ... (A operand of block q / 2,
+// K-step q % 2), in the layout of read_vt
+template <int D, int PAR>
+__device__ __forceinline__ void read_vt_parity(bf16x8 (&vf)[D / 16], const char *Vt, const RowCtx &c) {
+    const int hi = c.lane >> 5, kh = c.wave >> 1, l32 = c.lane & 31;
+#pragma unroll
+    for (int q = PAR; q < D / 16; q += 2) {
+        const int d = 32 * (q >> 1) + l32, ch = 4 * kh + 2 * (q & 1) + hi;
+        vf[q] = *reinterpret_cast<const bf16x8 *>(Vt + d * 128 + 16 * vt_slot(d, ch));
+    }
+}
+
 // The compute of one pipeline step for listed tile e, whose scores s_cur are formed, masked and
-// prepped (nbias): reads K(e+1) and V^T(e), forms S(e+1) -> s_nxt (masked) interleaved with
-// P(e) = exp2(...), then O += V^T(e) P(e)^T interleaved with the max tree of S(e+1), and the
-// lazy raise for S(e+1) (updates nbias).
+// prepped (nbias): reads K(e+1) and V^T(e), forms S(e+1) -> s_nxt (masked), computes
+// P(e) = exp2(...) and O += V^T(e) P(e)^T, and runs the lazy raise for S(e+1) (updates nbias).
+// Only a wave's own VALU work overlaps its MFMAs (the MFMAs of one wave and the VALU work of
+// another on the same SIMD do not co-execute), so the VALU work is spread over all MFMAs:
+//   score MFMAs of S(e+1)      <- exponentials of P(e) pairs 0..3, V^T operand reads;
+//   PV MFMAs of P pairs 0..3   <- exponentials of pairs 4..7;
+//   PV MFMAs of P pairs 4..7   <- max tree of S(e+1).
+// A pair's fma and exponentials are issued one slot ahead of its rounding, so no VALU op waits on
+// the one before it.
 template <int D>
 __device__ __forceinline__ void step_compute(WaveState<D> &st, const f32x16 &s_cur, f32x16 &s_nxt, float &nbias,
                                              const char *Kt, const char *Vt, int t_next, int v_next,
                                              const RowCtx &c) {
     constexpr int DC = D / 16;
-    constexpr int PAIRS_PER_MFMA = 8 / DC;  // exp pairs issued behind each score MFMA
+    constexpr int SPP = DC / 4;  // score MFMAs ahead of each of pairs 0..3
     bf16x8 kf[DC], vf[DC];
     read_k<D>(kf, Kt, c);
     __builtin_amdgcn_sched_barrier(0);
@@ -341,53 +349,67 @@ __device__ __forceinline__ void step_compute(WaveState<D> &st, const f32x16 &s_c
     f32x16 s = f32x16{};
     bf16x8 pb[2];
     float l = st.l_run;
-    // software pipeline over the 8 pairs of P(e): fma of pair k + 1 and exp of pair k are
-    // issued while pair k - 1 is rounded and summed, so no VALU op waits on its neighbour
     float x0 = fmaf(s_cur[0], c.scale_log2, nbias), x1 = fmaf(s_cur[1], c.scale_log2, nbias);
-    float e0 = 0.0f, e1 = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        if (k % PAIRS_PER_MFMA == 0) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k / PAIRS_PER_MFMA], st.qf[k / PAIRS_PER_MFMA], s, 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (k > 0) {
-            const bf16x2 pr = {static_cast<__bf16>(e0), static_cast<__bf16>(e1)};
-            l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
-            pb[(k - 1) >> 2][(2 * (k - 1)) & 7] = pr[0];
-            pb[(k - 1) >> 2][((2 * (k - 1)) & 7) + 1] = pr[1];
-        }
-        e0 = __builtin_amdgcn_exp2f(x0);
-        e1 = __builtin_amdgcn_exp2f(x1);
+    auto round_pair = [&](int k, float a, float b) {
+        const bf16x2 pr = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+        l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+        pb[k >> 2][(2 * k) & 7] = pr[0];
+        pb[k >> 2][((2 * k) & 7) + 1] = pr[1];
+    };
+    float p0 = 0.0f, p1 = 0.0f;  // exponentials of the last pair computed, not yet rounded
+    // exponentials of pair k, the fma of pair k + 1, and pair k - 1 rounded into pb and summed
+    // into l (in pair order, so l is the same sum whatever the MFMA placement); pair 3 is rounded
+    // on its own, ahead of the PV MFMAs that read it, so pair 4 does not round it again
+    auto next_pair = [&](int k) {
+        const float n0 = __builtin_amdgcn_exp2f(x0), n1 = __builtin_amdgcn_exp2f(x1);
         if (k < 7) {
             x0 = fmaf(s_cur[2 * k + 2], c.scale_log2, nbias);
             x1 = fmaf(s_cur[2 * k + 3], c.scale_log2, nbias);
         }
-        // V^T operands in two halves, into the registers the consumed K operands free
-        if (k == 3) read_vt_half<D>(vf, Vt, c, 0);
-        if (k == 5) read_vt_half<D>(vf, Vt, c, 1);
+        if (k > 0 && k != 4) round_pair(k - 1, p0, p1);
+        p0 = n0;
+        p1 = n1;
+    };
+    // score region: S(e+1), with pairs 0..3 of P(e) and the V^T operand reads behind it
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int m = 0; m < SPP; ++m) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k * SPP + m], st.qf[k * SPP + m], s, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        next_pair(k);
+        // V^T operands into the registers the consumed K operands free
+        if (k == 1) read_vt_parity<D, 0>(vf, Vt, c);
+        if (k == 2) read_vt_parity<D, 1>(vf, Vt, c);
         __builtin_amdgcn_sched_barrier(0);
     }
-    {
-        const bf16x2 pr = {static_cast<__bf16>(e0), static_cast<__bf16>(e1)};
-        l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
-        pb[1][6] = pr[0];
-        pb[1][7] = pr[1];
+    round_pair(3, p0, p1);  // pb[0] complete
+    __builtin_amdgcn_sched_barrier(0);
+    // PV of pairs 0..3 (pb[0]: the even K-steps), with the exponentials of pairs 4..7 behind it
+#pragma unroll
+    for (int k = 4; k < 8; ++k) {
+        const int qi = (k - 4) * (DC / 2) / 4;  // the even-q MFMA issued at this slot, if any
+        if (((k - 4) * (DC / 2)) % 4 == 0) {
+            st.acc_o[qi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[2 * qi], pb[0], st.acc_o[qi], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        next_pair(k);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    round_pair(7, p0, p1);  // pb[1] complete
     st.l_run = l;
     __builtin_amdgcn_sched_barrier(0);
-    // O += V^T(e) P(e)^T, with the max tree of S(e+1) behind the MFMAs (no branch inside this
-    // region: a branch would let the exponentials above sink past the scheduling barriers)
+    // PV of pairs 4..7 (pb[1]: the odd K-steps), with the max tree of S(e+1) behind it (no branch
+    // inside this region: a branch would let the exponentials above sink past the barriers)
     float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f;
 #pragma unroll
-    for (int q = 0; q < DC; ++q) {
-        st.acc_o[q >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[q], pb[q & 1], st.acc_o[q >> 1], 0, 0, 0);
+    for (int j = 0; j < DC / 2; ++j) {
+        st.acc_o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[2 * j + 1], pb[1], st.acc_o[j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        // six max3 steps spread over the DC MFMAs, starting behind the second
 #pragma unroll
         for (int x = 0; x < 6; ++x) {
-            const int slot = 1 + (x * (DC - 1)) / 6;
-            if (slot != q) continue;
+            if ((x * (DC / 2)) / 6 != j) continue;
             if (x == 0) m0 = max3f(s[0], s[1], s[2]);
             if (x == 1) m1 = max3f(s[3], s[4], s[5]);
             if (x == 2) m2 = max3f(s[6], s[7], s[8]);
