@@ -20,6 +20,18 @@ def _declared_functions():
     return sorted(set(re.findall(r"\b(sift_[a-z0-9_]+)\s*\(", text)))
 
 
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library every entry point raises: there is no CPU fallback."""
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "libsift.so"))
+    monkeypatch.setattr(B, "_LIB", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        B._lib()
+    lay = sift.Layout(req_num_docs=[1], doc_len=[64], question_len=[0], num_q_heads=1,
+                      num_kv_heads=1, head_dim=64)
+    with pytest.raises(RuntimeError, match="not built"):
+        lay.workspace_bytes()
+
+
 def test_library_exports_every_declared_symbol():
     lib = sift.library()
     declared = _declared_functions()
