@@ -42,7 +42,7 @@ def test_fused_random_small(seed):
     assert_close(out[valid], ref[valid], case.name)
 
 
-@pytest.mark.parametrize("cid", [2, 5])
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
 def test_fused_configs_same_as_csr(cid):
     _same_as_csr_path(config(cid))
 
