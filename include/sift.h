@@ -56,6 +56,10 @@
  * Asynchrony: work is enqueued on `stream` and the call returns without waiting
  * for it; results are ready when the stream reaches that point.  The library
  * never synchronises the device.
+ * Workspace: a call's workspace is its scratch (row-queue counters, V^T tiles,
+ * decode intermediates) until its stream has passed the call.  Calls that can
+ * run at the same time, e.g. on different streams, need separate workspaces;
+ * calls in order on one stream may share one.
  * Errors: every call validates its host-side arguments first and launches
  * nothing on error.  Nothing throws across the ABI.
  */
