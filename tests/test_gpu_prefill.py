@@ -24,6 +24,41 @@ def _full_check(case):
     return mx, mean
 
 
+def _row_raises(case, rp, ci, h, g, lazy_log2=8.0):
+    """How often the running tile max of row (h, g) rises by more than lazy_log2 (log2 units)
+    along its list: a property of the input, used to show that a case exercises the rescale."""
+    q = W.bf16_bits_to_f32(case.q[g * 64:(g + 1) * 64, h]).astype(np.float64)
+    kvh = h // (case.num_q_heads // case.num_kv_heads)
+    row = h * ((len(rp) - 1) // case.num_q_heads) + g
+    m, raises = None, 0
+    for t in ci[rp[row]:rp[row + 1]]:
+        k = W.bf16_bits_to_f32(case.k[t * 64:(t + 1) * 64, kvh]).astype(np.float64)
+        top = float(np.max(q @ k.T)) * case.scale / np.log(2.0)
+        if m is None:
+            m = top
+        elif top > m + lazy_log2:
+            m, raises = top, raises + 1
+    return raises
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_growing_scores_exercise_the_lazy_rescale(d):
+    """Keys scaled up along the sequence (x1 to x13), so the running max of a row rises by more
+    than the lazy threshold many times and O and l are rescaled mid-row.  With N(0, 1) inputs
+    that never happens after a row's first tile, so the other cases leave this path unexercised."""
+    case = W.make_case(f"growing-{d}", 70 + d, [4], [300, 256, 400, 200], [100], 4, 2, d,
+                       np.full((1, 4), 0.6), np.full((1, 4), 0.6))
+    n = case.k.shape[0]
+    grow = (1.0 + 12.0 * np.arange(n) / n).astype(np.float32)
+    k = W.bf16_bits_to_f32(case.k) * grow[:, None, None]
+    case = dataclasses.replace(case, k=W.f32_to_bf16_bits(k))
+    rp, ci = oracle.decode(case)
+    G = (len(rp) - 1) // case.num_q_heads
+    raises = [_row_raises(case, rp, ci, h, g) for h in range(case.num_q_heads) for g in range(G)]
+    assert sum(raises) >= 20 and max(raises) >= 2, f"the case must raise the max mid-row: {raises}"
+    _full_check(case)
+
+
 def test_prefill_tiny_config_fp32_inputs():
     """Config 1: fp32 Q/K/V, rounded to bf16 on the device, vs the oracle on the same rounding."""
     case = config(1)
