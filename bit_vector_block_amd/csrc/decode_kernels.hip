@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kCountThreads) void bits_prepass_kernel(
     int32_t *__restrict__ ca_prefix, int32_t *__restrict__ ca_list, int32_t *__restrict__ rowinfo) {
     if (!plan_ok(pv)) return;
     const int h = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const int ndocs = pv.num_docs, G = pv.num_tiles;
     int32_t *pref = ca_prefix + static_cast<int64_t>(h) * ndocs;
     int32_t *lst = ca_list + static_cast<int64_t>(h) * G;
