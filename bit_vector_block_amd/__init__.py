@@ -7,13 +7,17 @@ Hand-written HIP kernels behind the C ABI of include/sift.h:
   * ``sparse_prefill_bits`` -- the same attention with the decode fused in (reads the bits);
   * ``tile_masses`` / ``select_bits`` -- the offline encoder: per-tile softmax mass of the dense
                           attention, then top-p selection into LA/CA bits.
+What only the device can see (a plan of another layout, tile ids or CSR rows out of range) is
+reported in a device status word: ``device_status(workspace)``.
 This package is the ctypes binding (argument marshalling), the seeded synthetic
 workloads in ``workloads`` and the multi-layer stream orchestration in ``pipeline``.
 """
-from ._binding import (SIFT_BF16, SIFT_FP32, Layout, SiftError, decode_bits, default_scale,
-                       encode_masses_bytes, library, plan_upload, select_bits, sparse_prefill,
-                       sparse_prefill_bits, tile_masses)
+from ._binding import (SIFT_BF16, SIFT_DEVICE_OK, SIFT_DEVICE_PLAN_MISMATCH, SIFT_DEVICE_ROW_RANGE,
+                       SIFT_DEVICE_TILE_RANGE, SIFT_FP32, Layout, SiftError, decode_bits, default_scale,
+                       device_status, encode_masses_bytes, library, plan_upload, select_bits, sparse_prefill,
+                       sparse_prefill_bits, tile_masses, workspace)
 
 __all__ = ["Layout", "SiftError", "decode_bits", "sparse_prefill", "sparse_prefill_bits", "plan_upload",
-           "tile_masses", "select_bits", "encode_masses_bytes", "library", "default_scale", "SIFT_BF16",
-           "SIFT_FP32"]
+           "tile_masses", "select_bits", "encode_masses_bytes", "library", "default_scale", "workspace",
+           "device_status", "SIFT_BF16", "SIFT_FP32", "SIFT_DEVICE_OK", "SIFT_DEVICE_PLAN_MISMATCH",
+           "SIFT_DEVICE_TILE_RANGE", "SIFT_DEVICE_ROW_RANGE"]

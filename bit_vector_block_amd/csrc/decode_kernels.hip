@@ -29,11 +29,6 @@ namespace {
 constexpr int kCountThreads = 256;
 constexpr int kFillWaves = 4;
 
-__device__ inline bool plan_ok(const PlanView &pv) {
-    return pv.header[0] == static_cast<int32_t>(kPlanMagic) &&
-           static_cast<uint32_t>(pv.header[2]) == pv.fp_lo &&
-           static_cast<uint32_t>(pv.header[3]) == pv.fp_hi && pv.header[6] == pv.num_tiles;
-}
 
 // Number of set bits among bits [lo, hi] (inclusive) of a word array.
 __device__ inline int popcount_range(const uint32_t *vec, int lo, int hi) {
@@ -134,8 +129,11 @@ __device__ inline void head_ca_list(const PlanView &pv, const uint32_t *__restri
 __global__ __launch_bounds__(kCountThreads) void decode_count_kernel(
     PlanView pv, const uint32_t *__restrict__ la, const uint32_t *__restrict__ ca,
     int32_t *__restrict__ ca_prefix, int32_t *__restrict__ ca_list, int32_t *__restrict__ row_local,
-    int32_t *__restrict__ head_total) {
-    if (!plan_ok(pv)) return;
+    int32_t *__restrict__ head_total, int32_t *__restrict__ status) {
+    const bool ok = plan_ok(pv);
+    // the call's status word: written once, by this thread alone
+    if (blockIdx.x == 0 && threadIdx.x == 0) *status = ok ? SIFT_DEVICE_OK : SIFT_DEVICE_PLAN_MISMATCH;
+    if (!ok) return;
     const int h = blockIdx.x;
     const int tid = threadIdx.x;
     const int ndocs = pv.num_docs, G = pv.num_tiles;
@@ -160,8 +158,12 @@ __global__ __launch_bounds__(kCountThreads) void decode_count_kernel(
     if (tid == 0) head_total[h] = carry;
 }
 
-__global__ void zero_kernel(int32_t *p, int n) {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+// A batch without tiles: row_ptr = {0}, and the status word cleared.
+__global__ void empty_decode_kernel(int32_t *row_ptr, int32_t *status) {
+    if (threadIdx.x == 0) {
+        row_ptr[0] = 0;
+        *status = SIFT_DEVICE_OK;
+    }
 }
 
 __device__ inline int wave_sum(int x) {
@@ -174,12 +176,18 @@ __global__ __launch_bounds__(64 * kFillWaves) void decode_fill_kernel(
     const int32_t *__restrict__ ca_list, const int32_t *__restrict__ row_local,
     const int32_t *__restrict__ head_total, int32_t *__restrict__ row_ptr,
     int32_t *__restrict__ col_idx) {
-    if (!plan_ok(pv)) return;
     const int lane = threadIdx.x & 63;
-    const int G = pv.num_tiles, Hq = pv.num_q_heads;
+    const int G = pv.num_tiles, Hq = pv.num_q_heads;  // the host's layout, not read from the plan
     const int64_t nrows = static_cast<int64_t>(Hq) * G;
     const int64_t row = static_cast<int64_t>(blockIdx.x) * kFillWaves + (threadIdx.x >> 6);
     if (row >= nrows) return;  // whole wavefront leaves together
+    if (!plan_ok(pv)) {  // a plan of another layout: an empty CSR (the count kernel set the status)
+        if (lane == 0) {
+            row_ptr[row] = 0;
+            if (row == nrows - 1) row_ptr[nrows] = 0;
+        }
+        return;
+    }
     const int h = static_cast<int>(row / G), g = static_cast<int>(row % G);
 
     int partial = 0;
@@ -278,21 +286,21 @@ hipError_t launch_bits_prepass(const HostLayout &hl, const PlanView &pv, const u
 }
 
 hipError_t launch_decode(const HostLayout &hl, const PlanView &pv, const uint32_t *la,
-                         const uint32_t *ca, int32_t *row_ptr, int32_t *col_idx, void *workspace,
-                         hipStream_t stream) {
+                         const uint32_t *ca, int32_t *row_ptr, int32_t *col_idx, void *scratch,
+                         int32_t *status, hipStream_t stream) {
     const size_t a0 = (sizeof(int32_t) * size_t(hl.Hq) * size_t(hl.ndocs > 0 ? hl.ndocs : 1) + 255) & ~size_t(255);
     const size_t a1 = (sizeof(int32_t) * size_t(hl.Hq) * size_t(hl.G > 0 ? hl.G : 1) + 255) & ~size_t(255);
-    char *ws = static_cast<char *>(workspace);
+    char *ws = static_cast<char *>(scratch);
     int32_t *ca_prefix = reinterpret_cast<int32_t *>(ws);
     int32_t *row_local = reinterpret_cast<int32_t *>(ws + a0);
     int32_t *head_total = reinterpret_cast<int32_t *>(ws + a0 + a1);
     int32_t *ca_list = reinterpret_cast<int32_t *>(ws + a0 + a1 + ((sizeof(int32_t) * size_t(hl.Hq) + 255) & ~size_t(255)));
     if (hl.G == 0) {  // no rows: row_ptr[0] = 0
-        zero_kernel<<<1, 64, 0, stream>>>(row_ptr, 1);
+        empty_decode_kernel<<<1, 64, 0, stream>>>(row_ptr, status);
         return hipGetLastError();
     }
     decode_count_kernel<<<hl.Hq, kCountThreads, 0, stream>>>(pv, la, ca, ca_prefix, ca_list, row_local,
-                                                              head_total);
+                                                              head_total, status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nrows = int64_t(hl.Hq) * hl.G;

@@ -31,11 +31,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 
-__device__ inline bool plan_ok(const PlanView &pv) {
-    return pv.header[0] == static_cast<int32_t>(kPlanMagic) &&
-           static_cast<uint32_t>(pv.header[2]) == pv.fp_lo &&
-           static_cast<uint32_t>(pv.header[3]) == pv.fp_hi && pv.header[6] == pv.num_tiles;
-}
 
 __device__ inline int req_of_tile(const PlanView &pv, int g) {
     const int d = pv.tile_doc[g];
@@ -92,7 +87,7 @@ __device__ __forceinline__ void store_k_tile(const uint4 (&stage)[64 * (D / 8) /
 template <int D, int HPW>
 __device__ __forceinline__ void tile_mass_body(const PlanView &pv, const uint16_t *__restrict__ q,
                                                const uint16_t *__restrict__ k, int Hq, int Hkv, float scale_log2,
-                                               float *__restrict__ masses, int RT) {
+                                               float *__restrict__ masses, int RT, int32_t *__restrict__ status) {
     constexpr int NT = 128 * HPW;
     constexpr int KROW = 2 * D + 16;
     constexpr int CH = D / 8;              // 16-byte chunks per key row
@@ -100,7 +95,10 @@ __device__ __forceinline__ void tile_mass_body(const PlanView &pv, const uint16_
     static_assert(PER * NT == 64 * CH, "tile chunks split evenly");
     __shared__ __attribute__((aligned(16))) char Kt[2][64 * KROW];
     __shared__ float part[2][2 * HPW];
-    if (!plan_ok(pv)) return;
+    const bool ok = plan_ok(pv);
+    if (status != nullptr && blockIdx.x == 0 && threadIdx.x == 0)  // the call's one writer
+        *status = ok ? SIFT_DEVICE_OK : SIFT_DEVICE_PLAN_MISMATCH;
+    if (!ok) return;
     const int G = pv.num_tiles;
     const int group = Hq / Hkv, ngroups = group / HPW;
     // latest query tiles (the longest rows) first
@@ -206,16 +204,16 @@ __device__ __forceinline__ void tile_mass_body(const PlanView &pv, const uint16_
 template <int D, int HPW>
 __global__ __launch_bounds__(128 * HPW) __attribute__((amdgpu_waves_per_eu(2, 4))) void tile_mass_kernel(
     PlanView pv, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, int Hq, int Hkv, float scale_log2,
-    float *__restrict__ masses, int RT) {
-    tile_mass_body<D, HPW>(pv, q, k, Hq, Hkv, scale_log2, masses, RT);
+    float *__restrict__ masses, int RT, int32_t *__restrict__ status) {
+    tile_mass_body<D, HPW>(pv, q, k, Hq, Hkv, scale_log2, masses, RT, status);
 }
 
 // one q head per workgroup (odd groups): two wavefronts stage a whole tile each, so more registers
 template <int D>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 2))) void tile_mass_kernel_one(
     PlanView pv, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, int Hq, int Hkv, float scale_log2,
-    float *__restrict__ masses, int RT) {
-    tile_mass_body<D, 1>(pv, q, k, Hq, Hkv, scale_log2, masses, RT);
+    float *__restrict__ masses, int RT, int32_t *__restrict__ status) {
+    tile_mass_body<D, 1>(pv, q, k, Hq, Hkv, scale_log2, masses, RT, status);
 }
 
 // One wavefront: sort 64 (mass, index) pairs by decreasing mass, ties by increasing index.
@@ -272,10 +270,14 @@ constexpr int kSelectWaves = 4;
 __global__ __launch_bounds__(64 * kSelectWaves) void select_bits_kernel(PlanView pv, const float *__restrict__ masses,
                                                                         int RT, float p_la, float p_ca,
                                                                         uint32_t *__restrict__ la_out,
-                                                                        uint32_t *__restrict__ ca_out) {
+                                                                        uint32_t *__restrict__ ca_out,
+                                                                        int32_t *__restrict__ status) {
     __shared__ uint32_t la_words[72];  // T <= 64: at most 65 words
     __shared__ uint32_t ca_words[4];
-    if (!plan_ok(pv)) return;
+    const bool ok = plan_ok(pv);
+    if (status != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)  // the call's one writer
+        *status = ok ? SIFT_DEVICE_OK : SIFT_DEVICE_PLAN_MISMATCH;
+    if (!ok) return;
     const int G = pv.num_tiles;
     const int h = blockIdx.x, d = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = pv.doc_tiles[d], t0 = pv.doc_first[d], b = pv.doc_req[d];
@@ -325,32 +327,32 @@ __global__ __launch_bounds__(64 * kSelectWaves) void select_bits_kernel(PlanView
 }  // namespace
 
 hipError_t launch_tile_masses(const HostLayout &hl, const PlanView &pv, const uint16_t *q, const uint16_t *k,
-                              float scale, float *masses, int RT, hipStream_t stream) {
+                              float scale, float *masses, int RT, int32_t *status, hipStream_t stream) {
     if (hl.G == 0) return hipSuccess;
     const int group = hl.Hq / hl.Hkv;
     const int hpw = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
     const unsigned grid = static_cast<unsigned>(int64_t(hl.Hkv) * (group / hpw) * hl.G);
     const float sl = scale * 1.4426950408889634f;
 #define SIFT_TILE_MASS(DD, HH) \
-    tile_mass_kernel<DD, HH><<<grid, 128 * HH, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT)
+    tile_mass_kernel<DD, HH><<<grid, 128 * HH, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT, status)
     if (hl.D == 128) {
         if (hpw == 4) SIFT_TILE_MASS(128, 4);
         else if (hpw == 2) SIFT_TILE_MASS(128, 2);
-        else tile_mass_kernel_one<128><<<grid, 128, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT);
+        else tile_mass_kernel_one<128><<<grid, 128, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT, status);
     } else {
         if (hpw == 4) SIFT_TILE_MASS(64, 4);
         else if (hpw == 2) SIFT_TILE_MASS(64, 2);
-        else tile_mass_kernel_one<64><<<grid, 128, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT);
+        else tile_mass_kernel_one<64><<<grid, 128, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT, status);
     }
 #undef SIFT_TILE_MASS
     return hipGetLastError();
 }
 
 hipError_t launch_select_bits(const HostLayout &hl, const PlanView &pv, const float *masses, int RT, float p_la,
-                              float p_ca, uint32_t *la_out, uint32_t *ca_out, hipStream_t stream) {
+                              float p_ca, uint32_t *la_out, uint32_t *ca_out, int32_t *status, hipStream_t stream) {
     if (hl.ndocs == 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(hl.Hq), static_cast<unsigned>(hl.ndocs));
-    select_bits_kernel<<<grid, 64 * kSelectWaves, 0, stream>>>(pv, masses, RT, p_la, p_ca, la_out, ca_out);
+    select_bits_kernel<<<grid, 64 * kSelectWaves, 0, stream>>>(pv, masses, RT, p_la, p_ca, la_out, ca_out, status);
     return hipGetLastError();
 }
 

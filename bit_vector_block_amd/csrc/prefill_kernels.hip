@@ -68,11 +68,6 @@ constexpr float kLazyLog2 = 8.0f;
 constexpr int kXcds = 8;
 constexpr int kPersistentPerXcd = 64;  // 2 workgroups on each of the 32 CUs of an XCD
 
-__device__ inline bool plan_ok(const PlanView &pv) {
-    return pv.header[0] == static_cast<int32_t>(kPlanMagic) &&
-           static_cast<uint32_t>(pv.header[2]) == pv.fp_lo &&
-           static_cast<uint32_t>(pv.header[3]) == pv.fp_hi && pv.header[6] == pv.num_tiles;
-}
 
 template <int D>
 struct Cfg {
@@ -440,18 +435,30 @@ struct TileList {
     bool raw1;   // c1 still holds raw ids
 };
 
+// Marks a list position past the row's last entry (no CSR value can be it: they are checked
+// against [0, G) and G < 2^25).
+constexpr int kNoEntry = INT32_MIN;
+
 // raw tile ids of entries [base, base + 64) of a row starting at CSR offset e0 with n entries
-// (-1 past the end); no use of the loaded value here, so nothing waits for it
+// (kNoEntry past the end); no use of the loaded value here, so nothing waits for it
 __device__ __forceinline__ int load_ids(int base, int n, int e0, const int32_t *__restrict__ col_idx, int lane) {
     const int j = base + lane;
-    return j < n ? col_idx[e0 + j] : -1;
+    return j < n ? col_idx[e0 + j] : kNoEntry;
 }
 
-// out-of-range entries are skipped (masked)
+// out-of-range entries (and kNoEntry) are skipped (masked)
 __device__ __forceinline__ int valid_id(int x, int G) { return (x >= 0 && x < G) ? x : -1; }
 
-// a raw tile id packed with its valid-token count (1..64)
-__device__ __forceinline__ int with_valid(int x, int G, const int32_t *__restrict__ tile_valid) {
+// Raise flag bits in the call's status word, once per wavefront (`raise` is per lane).
+__device__ __forceinline__ void flag_status(bool raise, int flags, int *__restrict__ status) {
+    const uint64_t m = __ballot(raise);
+    if (m != 0 && (threadIdx.x & 63) == __builtin_ctzll(m)) atomicOr(status, flags);
+}
+
+// a raw tile id packed with its valid-token count (1..64); a listed id outside [0, G) is skipped
+// and flagged in the status word
+__device__ __forceinline__ int with_valid(int x, int G, const int32_t *__restrict__ tile_valid, int *status) {
+    flag_status(x != kNoEntry && (x < 0 || x >= G), SIFT_DEVICE_TILE_RANGE, status);
     x = valid_id(x, G);
     return x >= 0 ? (x | ((tile_valid[x] - 1) << 25)) : -1;
 }
@@ -476,14 +483,14 @@ template <bool FUSED>
 __device__ __forceinline__ void advance_chunk(TileList &L, int i, int mw, int G,
                                               const int32_t *__restrict__ col_idx,
                                               const int32_t *__restrict__ ca_list, const uint32_t *__restrict__ la,
-                                              const int32_t *__restrict__ tile_valid, int lane) {
+                                              const int32_t *__restrict__ tile_valid, int lane, int *status) {
     if ((i >> 6) != L.c) {  // entry i entered chunk c + 1: shift, fetch chunk c + 2's ids
         L.c += 1;
         L.c0 = L.c1;
         L.c1 = chunk_ids<FUSED>(64 * (L.c + 1), meta_of<FUSED>(mw), col_idx, ca_list, la, lane);
         L.raw1 = true;
     } else if (L.raw1) {  // one step later: their valid counts
-        L.c1 = with_valid(L.c1, G, tile_valid);
+        L.c1 = with_valid(L.c1, G, tile_valid, status);
         L.raw1 = false;
     }
 }
@@ -529,6 +536,15 @@ __device__ __forceinline__ RowMeta meta_of(int w) {
     return m;
 }
 
+// CSR path: a row whose [row_ptr[r], row_ptr[r + 1]) is not inside [0, col_entries] is read as
+// empty and flagged in the status word, so no entry outside the caller's col_idx is read.
+__device__ __forceinline__ int checked_meta(int w, int64_t col_entries, int *status) {
+    const int e0 = __builtin_amdgcn_readlane(w, 0), e1 = __builtin_amdgcn_readlane(w, 1);
+    const bool ok = e0 >= 0 && e1 >= e0 && static_cast<int64_t>(e1) <= col_entries;  // uniform
+    if (!ok && (threadIdx.x & 63) == 0) atomicOr(status, SIFT_DEVICE_ROW_RANGE);
+    return ok ? w : 0;
+}
+
 // Fused: lane j gets word j of the row's LA bit range (at most 64 words, checked on the host).
 __device__ __forceinline__ uint32_t load_la_words(const RowMeta &m, const uint32_t *__restrict__ la, int lane) {
     if (m.ca_n < 0) return 0u;
@@ -536,13 +552,14 @@ __device__ __forceinline__ uint32_t load_la_words(const RowMeta &m, const uint32
     return (w0 + lane <= w1) ? la[m.la_word + w0 + lane] : 0u;
 }
 
-// Fused: raw tile ids of entries [base, base + 64) of a row; law = load_la_words of the row.
+// Fused: raw tile ids of entries [base, base + 64) of a row (kNoEntry past its end); law =
+// load_la_words of the row.
 // A CA entry is a load from the request's page list (not waited for here); an LA entry is the
 // k-th set bit of the row's LA range, found from a prefix sum of the per-lane popcounts.
 __device__ __forceinline__ int gen_ids(int base, const RowMeta &m, uint32_t law, const int32_t *__restrict__ ca_list,
                                        int lane) {
     const int e = base + lane;
-    if (m.ca_n < 0) return e < m.n ? m.t0 + e : -1;  // question row: a dense range
+    if (m.ca_n < 0) return e < m.n ? m.t0 + e : kNoEntry;  // question row: a dense range
     const int w0 = m.la_lo >> 5, nw = ((m.la_lo + m.r) >> 5) - w0 + 1;
     uint32_t x = lane < nw ? law : 0u;
     if (lane == 0) x &= ~0u << (m.la_lo & 31);
@@ -577,7 +594,7 @@ __device__ __forceinline__ int gen_ids(int base, const RowMeta &m, uint32_t law,
             pos += width;
         }
     }
-    int t = (e < m.n) ? m.t0 + (32 * (w0 + ic) + pos - m.la_lo) : -1;
+    int t = (e < m.n) ? m.t0 + (32 * (w0 + ic) + pos - m.la_lo) : kNoEntry;
     if (e < m.ca_n) t = ca_list[m.ca_base + e];
     return t;
 }
@@ -710,8 +727,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     PlanView pv, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ vt, const int32_t *__restrict__ row_ptr,
     const int32_t *__restrict__ col_idx, const int32_t *__restrict__ rowinfo,
-    const int32_t *__restrict__ ca_list, const uint32_t *__restrict__ la_bits, float scale, float scale_log2,
-    float lazy_raw, float *__restrict__ out, float *__restrict__ lse, int Hq, int Hkv, Queues Qs,
+    const int32_t *__restrict__ ca_list, const uint32_t *__restrict__ la_bits, int64_t col_entries, float scale,
+    float scale_log2, float lazy_raw, float *__restrict__ out, float *__restrict__ lse, int Hq, int Hkv, Queues Qs,
     int *__restrict__ counters) {
     using C = Cfg<D>;
     constexpr int DB = D / 32;
@@ -721,11 +738,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ __attribute__((aligned(1024))) char kb1[C::KBYTES];
     __shared__ __attribute__((aligned(1024))) char vb0[C::VBYTES];
     __shared__ __attribute__((aligned(1024))) char vb1[C::VBYTES];
-    __shared__ int s_row;  // the row the claiming lane resolved for the workgroup
+    // the row the claiming lane resolved for the workgroup, in slot (claim number & 1): a slot is
+    // written again only after the barrier that follows every wave's read of it
+    __shared__ int s_row[2];
     static_assert(HB * 16 * 64 * 4 * 2 <= C::VBYTES && HB * 16 * 64 * 4 * 2 + 1024 <= C::KBYTES,
                   "merge exchange fits kb1 | vb1");
+    int *status = counters + kStatusWord;  // cleared by the V transpose before this kernel
 
-    if (!plan_ok(pv)) return;
+    if (!plan_ok(pv)) {  // a plan of another layout: nothing is computed or written but the flag
+        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(status, SIFT_DEVICE_PLAN_MISMATCH);
+        return;
+    }
     const int G = pv.num_tiles;
     const int group = Hq / Hkv;
     const int64_t N = static_cast<int64_t>(G) * kTile;
@@ -742,11 +765,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     int pending = 0;  // claimer: a claim kept in flight one row ahead of its use
     if (claimer) {
-        s_row = resolve_claim(counters, Qs, cq, home, atomicAdd(&counters[home], 1));
+        s_row[0] = resolve_claim(counters, Qs, cq, home, atomicAdd(&counters[home], 1));
         pending = atomicAdd(&counters[cq % kXcds], 1);
     }
     lds_barrier();
-    int row_idx = s_row;
+    int row_idx = s_row[0];
+    int claim_no = 1;  // claims resolved so far (uniform)
     if (row_idx < 0) return;
 
     // the first row's Q, list metadata and first tile ids
@@ -754,6 +778,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     WaveState<D> st;
     load_q<D>(st, q, rid, Hq, qi, hi);
     int mw = meta_word<FUSED>(static_cast<int64_t>(rid.h) * G + rid.g, row_ptr, rowinfo, lane);
+    if constexpr (!FUSED) mw = checked_meta(mw, col_entries, status);
     int n = meta_of<FUSED>(mw).n;
     // raw tile ids of the row's entries 0..63
     int ids0 = chunk_ids<FUSED>(0, meta_of<FUSED>(mw), col_idx, ca_list, la_bits, lane);
@@ -781,13 +806,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         int nids = -1;    // stage 2: raw tile ids of the next row's entries 0..63 (stage 1, fused: its LA words)
         int nstage = 0;   // 0: nothing fetched, 1: (fused) LA words in flight, 2: ids in flight
         auto resolve_next = [&]() {  // every wave; includes a workgroup barrier
+            const int slot = claim_no & 1;
             if (claimer) {
                 const int r = resolve_claim(counters, Qs, cq, home, pending);
-                s_row = r;
+                s_row[slot] = r;
                 if (r >= 0) pending = atomicAdd(&counters[cq % kXcds], 1);
             }
             lds_barrier();
-            next_idx = s_row;
+            next_idx = s_row[slot];
+            ++claim_no;
             if (next_idx >= 0) {
                 const RowId nid = row_of(next_idx, G, group);
                 nmw = meta_word<FUSED>(static_cast<int64_t>(nid.h) * G + nid.g, row_ptr, rowinfo, lane);
@@ -805,7 +832,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 }
                 nids = gen_ids(0, nm, static_cast<uint32_t>(nids), ca_list, lane);
             } else {
-                nids = load_ids(0, nm.n, nm.e0, col_idx, lane);
+                nmw = checked_meta(nmw, col_entries, status);  // before any col_idx read of the row
+                const RowMeta cm = meta_of<FUSED>(nmw);
+                nids = load_ids(0, cm.n, cm.e0, col_idx, lane);
             }
             nstage = 2;
         };
@@ -824,7 +853,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             if (n > 1) load_k_tile<D>(k_tile_base<D>(ctx, valid_id(__builtin_amdgcn_readlane(ids0, 1), G)), kb1, wave, off.k);
             TileList L;
             L.c = 0;
-            L.c0 = with_valid(ids0, G, pv.tile_valid);
+            L.c0 = with_valid(ids0, G, pv.tile_valid, status);
             L.c1 = n > 64 ? chunk_ids<FUSED>(64, meta_of<FUSED>(mw), col_idx, ca_list, la_bits, lane) : -1;
             L.raw1 = n > 64;
             int t0, v0, t1, v1;
@@ -839,7 +868,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // role: step e: wait + barrier; K(e+2) -> free K buffer, V(e+1) -> free V buffer; compute
             int t_a = t1, v_a = v1;  // entry i + 1
             while (i + 1 < n) {
-                advance_chunk<FUSED>(L, i, mw, G, col_idx, ca_list, la_bits, pv.tile_valid, lane);
+                advance_chunk<FUSED>(L, i, mw, G, col_idx, ca_list, la_bits, pv.tile_valid, lane, status);
                 int t_b, v_b;
                 list_entry(L, i + 2, t_b, v_b);
                 wait_vmcnt_le(0);
@@ -853,7 +882,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 t_a = t_b;
                 v_a = v_b;
                 if (i + 1 >= n) break;
-                advance_chunk<FUSED>(L, i, mw, G, col_idx, ca_list, la_bits, pv.tile_valid, lane);
+                advance_chunk<FUSED>(L, i, mw, G, col_idx, ca_list, la_bits, pv.tile_valid, lane, status);
                 list_entry(L, i + 2, t_b, v_b);
                 wait_vmcnt_le(0);
                 __builtin_amdgcn_s_barrier();
@@ -945,9 +974,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // LDS so that both the 2D-byte row reads and the 128-byte V^T row writes are whole rows.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const T *__restrict__ v, uint16_t *__restrict__ vt,
-                                                          int Hkv, int64_t N, int *__restrict__ counters) {
-    // the attention kernel that follows on the stream claims rows from these counters
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kXcds) counters[threadIdx.x] = 0;
+                                                          int Hkv, int64_t N, int *__restrict__ header) {
+    // the attention kernel that follows on the stream claims rows from the counters and raises
+    // flags in the status word: both start at zero for every call
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
+        if (threadIdx.x < kXcds) header[threadIdx.x] = 0;
+        if (threadIdx.x == 64) header[kStatusWord] = 0;
+    }
     constexpr int LD = D + 2;  // padded LDS row (bf16 elements): column reads hit distinct banks
     constexpr int CH = D / 8;  // 8-element chunks per token row
     __shared__ uint16_t tile[64 * LD];
@@ -1006,26 +1039,26 @@ hipError_t launch_cast_bf16(const float *src, uint16_t *dst, int64_t n, hipStrea
     return hipGetLastError();
 }
 
-hipError_t launch_transpose_v(const HostLayout &hl, const void *v, bool fp32, uint16_t *vt, int *counters,
+hipError_t launch_transpose_v(const HostLayout &hl, const void *v, bool fp32, uint16_t *vt, int *header,
                               hipStream_t stream) {
     if (hl.G == 0) return hipSuccess;
     const int64_t N = int64_t(hl.G) * kTile;
     const dim3 grid(static_cast<unsigned>(hl.G), static_cast<unsigned>(hl.Hkv));
     if (hl.D == 128) {
-        if (fp32) transpose_v_kernel<128, float><<<grid, 256, 0, stream>>>(static_cast<const float *>(v), vt, hl.Hkv, N, counters);
-        else transpose_v_kernel<128, __bf16><<<grid, 256, 0, stream>>>(static_cast<const __bf16 *>(v), vt, hl.Hkv, N, counters);
+        if (fp32) transpose_v_kernel<128, float><<<grid, 256, 0, stream>>>(static_cast<const float *>(v), vt, hl.Hkv, N, header);
+        else transpose_v_kernel<128, __bf16><<<grid, 256, 0, stream>>>(static_cast<const __bf16 *>(v), vt, hl.Hkv, N, header);
     } else {
-        if (fp32) transpose_v_kernel<64, float><<<grid, 256, 0, stream>>>(static_cast<const float *>(v), vt, hl.Hkv, N, counters);
-        else transpose_v_kernel<64, __bf16><<<grid, 256, 0, stream>>>(static_cast<const __bf16 *>(v), vt, hl.Hkv, N, counters);
+        if (fp32) transpose_v_kernel<64, float><<<grid, 256, 0, stream>>>(static_cast<const float *>(v), vt, hl.Hkv, N, header);
+        else transpose_v_kernel<64, __bf16><<<grid, 256, 0, stream>>>(static_cast<const __bf16 *>(v), vt, hl.Hkv, N, header);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_prefill(const HostLayout &hl, const PlanView &pv, const uint16_t *q,
                           const uint16_t *k, const uint16_t *vt, const int32_t *row_ptr,
-                          const int32_t *col_idx, const int32_t *rowinfo, const int32_t *ca_list,
-                          const uint32_t *la_bits, float scale, float *out, float *lse, int *counters,
-                          hipStream_t stream) {
+                          const int32_t *col_idx, int64_t col_entries, const int32_t *rowinfo,
+                          const int32_t *ca_list, const uint32_t *la_bits, float scale, float *out, float *lse,
+                          int *header, hipStream_t stream) {
     const bool fused = rowinfo != nullptr;
     const int64_t rows = int64_t(hl.Hq) * hl.G;
     if (rows == 0) return hipSuccess;
@@ -1049,8 +1082,9 @@ hipError_t launch_prefill(const HostLayout &hl, const PlanView &pv, const uint16
     const unsigned grid = static_cast<unsigned>(per_xcd) * kXcds;
 #define SIFT_LAUNCH(DD, FF)                                                                              \
     sparse_prefill_kernel<DD, FF><<<grid, kThreads, 0, stream>>>(pv, q, k, vt, row_ptr, col_idx, rowinfo,  \
-                                                                 ca_list, la_bits, scale, scale_log2,    \
-                                                                 lazy_raw, out, lse, hl.Hq, hl.Hkv, Qs, counters)
+                                                                 ca_list, la_bits, col_entries, scale,   \
+                                                                 scale_log2, lazy_raw, out, lse, hl.Hq,  \
+                                                                 hl.Hkv, Qs, header)
     if (hl.D == 128) {
         if (fused) SIFT_LAUNCH(128, true);
         else SIFT_LAUNCH(128, false);

@@ -180,23 +180,22 @@ PlanView plan_view(const HostLayout &hl, const void *d_plan) {
     return v;
 }
 
-// Decode scratch: ca_prefix [Hq][ndocs], row_local [Hq][G], head_total [Hq].
-// Decode scratch: ca_prefix [Hq][ndocs], row offsets [Hq][G], head totals [Hq], CA page lists
-// [Hq][G] (int32).
+// Decode workspace: the header, then ca_prefix [Hq][ndocs], row offsets [Hq][G], head totals
+// [Hq], CA page lists [Hq][G] (int32).
 size_t decode_workspace_bytes(const HostLayout &hl) {
-    return align256(sizeof(int32_t) * size_t(hl.Hq) * size_t(std::max(hl.ndocs, 1))) +
+    return kWorkspaceHeader + align256(sizeof(int32_t) * size_t(hl.Hq) * size_t(std::max(hl.ndocs, 1))) +
            align256(sizeof(int32_t) * size_t(hl.Hq) * size_t(std::max(hl.G, 1))) +
            align256(sizeof(int32_t) * size_t(hl.Hq)) +
            align256(sizeof(int32_t) * size_t(hl.Hq) * size_t(std::max(hl.G, 1)));
 }
 
-// Prefill scratch: 256 bytes of row-queue counters, V^T (bf16 tiles [Hkv][G][D][64]); for SIFT_FP32
-// inputs the bf16 copies of Q and K follow.  The fused path (no CSR) appends its pre-pass
-// tables: ca_prefix [Hq][ndocs], ca_list [Hq][G], rowinfo [Hq][G][8] (int32).
-constexpr size_t kCounterBytes = 256;
+// Prefill workspace: the header (row-queue counters, status word), V^T (bf16 tiles
+// [Hkv][G][D][64]); for SIFT_FP32 inputs the bf16 copies of Q and K follow.  The fused path (no
+// CSR) appends its pre-pass tables: ca_prefix [Hq][ndocs], ca_list [Hq][G], rowinfo [Hq][G][8]
+// (int32).
 static size_t prefill_workspace_bytes(const HostLayout &hl, sift_dtype dtype) {
     const size_t N = size_t(hl.G) * kTile;
-    const size_t vt = kCounterBytes + align256(2 * N * hl.Hkv * hl.D);
+    const size_t vt = kWorkspaceHeader + align256(2 * N * hl.Hkv * hl.D);
     if (dtype != SIFT_FP32) return vt;
     return vt + align256(2 * N * hl.Hq * hl.D) + align256(2 * N * hl.Hkv * hl.D);
 }
@@ -212,7 +211,7 @@ using namespace sift;
 
 extern "C" {
 
-int32_t sift_abi_version(void) { return (1 << 16) | 0; }
+int32_t sift_abi_version(void) { return (2 << 16) | 0; }
 
 const char *sift_status_string(sift_status s) {
     switch (s) {
@@ -295,22 +294,25 @@ sift_status sift_decode_bits(const sift_layout *layout, const void *d_plan, cons
     if (col_capacity < hl.max_nnz) return SIFT_ERR_CAPACITY;
     if (!d_workspace || workspace_bytes < decode_workspace_bytes(hl)) return SIFT_ERR_CAPACITY;
     const PlanView pv = plan_view(hl, d_plan);
-    if (launch_decode(hl, pv, d_la, d_ca, d_row_ptr, d_col_idx, d_workspace, stream) != hipSuccess)
+    char *ws = static_cast<char *>(d_workspace);
+    if (launch_decode(hl, pv, d_la, d_ca, d_row_ptr, d_col_idx, ws + kWorkspaceHeader,
+                      reinterpret_cast<int32_t *>(ws) + kStatusWord, stream) != hipSuccess)
         return SIFT_ERR_HIP;
     return SIFT_OK;
 }
 
 sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan, const void *d_q,
                                 const void *d_k, const void *d_v, sift_dtype dtype,
-                                const int32_t *d_row_ptr, const int32_t *d_col_idx, float scale,
-                                float *d_out, float *d_lse, void *d_workspace,
+                                const int32_t *d_row_ptr, const int32_t *d_col_idx, int64_t col_entries,
+                                float scale, float *d_out, float *d_lse, void *d_workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
     HostLayout hl;
     sift_status st = build_layout(layout, &hl);
     if (st != SIFT_OK) return st;
     if (dtype != SIFT_BF16 && dtype != SIFT_FP32) return SIFT_ERR_INVALID;
     if (hl.G == 0) return SIFT_OK;
-    if (!d_plan || !d_q || !d_k || !d_v || !d_row_ptr || !d_col_idx || !d_out)
+    if (!d_plan || !d_q || !d_k || !d_v || !d_row_ptr || !d_out || col_entries < 0 ||
+        (col_entries > 0 && !d_col_idx))
         return SIFT_ERR_INVALID;
     // Q/K/V are read and O written in 16-byte vectors
     auto aligned16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
@@ -327,10 +329,10 @@ sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan, c
     const int64_t N = int64_t(hl.G) * kTile;
     const int64_t nq = N * hl.Hq * hl.D, nkv = N * hl.Hkv * hl.D;
     char *ws = static_cast<char *>(d_workspace);
-    int *counters = reinterpret_cast<int *>(ws);
-    uint16_t *vt = reinterpret_cast<uint16_t *>(ws + kCounterBytes);
+    int *header = reinterpret_cast<int *>(ws);
+    uint16_t *vt = reinterpret_cast<uint16_t *>(ws + kWorkspaceHeader);
     if (dtype == SIFT_FP32) {
-        char *ws2 = ws + kCounterBytes + align256(2 * size_t(nkv));
+        char *ws2 = ws + kWorkspaceHeader + align256(2 * size_t(nkv));
         uint16_t *qb = reinterpret_cast<uint16_t *>(ws2);
         uint16_t *kb = reinterpret_cast<uint16_t *>(ws2 + align256(2 * size_t(nq)));
         if (launch_cast_bf16(static_cast<const float *>(d_q), qb, nq, stream) != hipSuccess ||
@@ -339,9 +341,9 @@ sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan, c
         q = qb;
         k = kb;
     }
-    if (launch_transpose_v(hl, d_v, dtype == SIFT_FP32, vt, counters, stream) != hipSuccess ||
-        launch_prefill(hl, pv, q, k, vt, d_row_ptr, d_col_idx, nullptr, nullptr, nullptr, scale, d_out, d_lse,
-                       counters, stream) != hipSuccess)
+    if (launch_transpose_v(hl, d_v, dtype == SIFT_FP32, vt, header, stream) != hipSuccess ||
+        launch_prefill(hl, pv, q, k, vt, d_row_ptr, d_col_idx, col_entries, nullptr, nullptr, nullptr, scale,
+                       d_out, d_lse, header, stream) != hipSuccess)
         return SIFT_ERR_HIP;
     return SIFT_OK;
 }
@@ -374,10 +376,10 @@ sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_pl
     const int64_t N = int64_t(hl.G) * kTile;
     const int64_t nq = N * hl.Hq * hl.D, nkv = N * hl.Hkv * hl.D;
     char *ws = static_cast<char *>(d_workspace);
-    int *counters = reinterpret_cast<int *>(ws);
-    uint16_t *vt = reinterpret_cast<uint16_t *>(ws + kCounterBytes);
+    int *header = reinterpret_cast<int *>(ws);
+    uint16_t *vt = reinterpret_cast<uint16_t *>(ws + kWorkspaceHeader);
     if (dtype == SIFT_FP32) {
-        char *ws2 = ws + kCounterBytes + align256(2 * size_t(nkv));
+        char *ws2 = ws + kWorkspaceHeader + align256(2 * size_t(nkv));
         uint16_t *qb = reinterpret_cast<uint16_t *>(ws2);
         uint16_t *kb = reinterpret_cast<uint16_t *>(ws2 + align256(2 * size_t(nq)));
         if (launch_cast_bf16(static_cast<const float *>(d_q), qb, nq, stream) != hipSuccess ||
@@ -392,9 +394,9 @@ sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_pl
     int32_t *ca_list = reinterpret_cast<int32_t *>(tb + align256(4 * size_t(hl.Hq) * size_t(hl.ndocs > 0 ? hl.ndocs : 1)));
     int32_t *rowinfo = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ca_list) + align256(4 * rows));
     if (launch_bits_prepass(hl, pv, d_la, d_ca, ca_prefix, ca_list, rowinfo, stream) != hipSuccess ||
-        launch_transpose_v(hl, d_v, dtype == SIFT_FP32, vt, counters, stream) != hipSuccess ||
-        launch_prefill(hl, pv, q, k, vt, nullptr, nullptr, rowinfo, ca_list, d_la, scale, d_out, d_lse,
-                       counters, stream) != hipSuccess)
+        launch_transpose_v(hl, d_v, dtype == SIFT_FP32, vt, header, stream) != hipSuccess ||
+        launch_prefill(hl, pv, q, k, vt, nullptr, nullptr, 0, rowinfo, ca_list, d_la, scale, d_out, d_lse,
+                       header, stream) != hipSuccess)
         return SIFT_ERR_HIP;
     return SIFT_OK;
 }
@@ -406,7 +408,8 @@ size_t sift_encode_masses_bytes(const sift_layout *layout) {
 }
 
 sift_status sift_tile_masses(const sift_layout *layout, const void *d_plan, const void *d_q, const void *d_k,
-                             float scale, float *d_masses, size_t masses_bytes, hipStream_t stream) {
+                             float scale, float *d_masses, size_t masses_bytes, int32_t *d_status,
+                             hipStream_t stream) {
     HostLayout hl;
     sift_status st = build_layout(layout, &hl);
     if (st != SIFT_OK) return st;
@@ -419,14 +422,14 @@ sift_status sift_tile_masses(const sift_layout *layout, const void *d_plan, cons
     if (masses_bytes < sift_encode_masses_bytes(layout)) return SIFT_ERR_CAPACITY;
     const PlanView pv = plan_view(hl, d_plan);
     if (launch_tile_masses(hl, pv, static_cast<const uint16_t *>(d_q), static_cast<const uint16_t *>(d_k), scale,
-                           d_masses, static_cast<int>(hl.max_req_tiles), stream) != hipSuccess)
+                           d_masses, static_cast<int>(hl.max_req_tiles), d_status, stream) != hipSuccess)
         return SIFT_ERR_HIP;
     return SIFT_OK;
 }
 
 sift_status sift_select_bits(const sift_layout *layout, const void *d_plan, const float *d_masses,
                              size_t masses_bytes, float p_la, float p_ca, uint32_t *d_la, uint32_t *d_ca,
-                             hipStream_t stream) {
+                             int32_t *d_status, hipStream_t stream) {
     HostLayout hl;
     sift_status st = build_layout(layout, &hl);
     if (st != SIFT_OK) return st;
@@ -436,8 +439,18 @@ sift_status sift_select_bits(const sift_layout *layout, const void *d_plan, cons
     if (hl.max_doc_tiles > 64) return SIFT_ERR_UNSUPPORTED;  // one lane per candidate tile
     if (masses_bytes < sift_encode_masses_bytes(layout)) return SIFT_ERR_CAPACITY;
     const PlanView pv = plan_view(hl, d_plan);
-    if (launch_select_bits(hl, pv, d_masses, static_cast<int>(hl.max_req_tiles), p_la, p_ca, d_la, d_ca, stream) !=
-        hipSuccess)
+    if (launch_select_bits(hl, pv, d_masses, static_cast<int>(hl.max_req_tiles), p_la, p_ca, d_la, d_ca, d_status,
+                           stream) != hipSuccess)
+        return SIFT_ERR_HIP;
+    return SIFT_OK;
+}
+
+sift_status sift_device_status(const void *d_workspace, size_t workspace_bytes, int32_t *h_flags,
+                               hipStream_t stream) {
+    if (!d_workspace || !h_flags) return SIFT_ERR_INVALID;
+    if (workspace_bytes < kWorkspaceHeader) return SIFT_ERR_CAPACITY;
+    const int32_t *word = static_cast<const int32_t *>(d_workspace) + kStatusWord;
+    if (hipMemcpyAsync(h_flags, word, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess)
         return SIFT_ERR_HIP;
     return SIFT_OK;
 }

@@ -14,6 +14,12 @@ constexpr int kTile = 64;
 constexpr uint32_t kPlanMagic = 0x54464953u;  // "SIFT"
 constexpr int kHeaderWords = 16;
 
+// Every workspace starts with a 256-byte header: int32 words 0..7 are the attention kernel's
+// row-queue counters, word kStatusWord holds the sift_device_flag bits of the last call that
+// used the workspace (read with sift_device_status).
+constexpr size_t kWorkspaceHeader = 256;
+constexpr int kStatusWord = 32;
+
 // Device view of an uploaded plan.  Every array lives inside the plan buffer.
 struct PlanView {
     const int32_t *header;      // [16]: magic, version, fp_lo, fp_hi, R, Ndocs, G, Hq, ...
@@ -33,6 +39,14 @@ struct PlanView {
     uint32_t fp_lo, fp_hi;      // fingerprint the host expects
     int32_t num_requests, num_docs, num_tiles, num_q_heads;
 };
+
+// Device check that an uploaded plan belongs to the layout the host validated: the plan header's
+// magic, fingerprint and tile count against the host's values carried in `pv`.
+__device__ inline bool plan_ok(const PlanView &pv) {
+    return pv.header[0] == static_cast<int32_t>(kPlanMagic) &&
+           static_cast<uint32_t>(pv.header[2]) == pv.fp_lo &&
+           static_cast<uint32_t>(pv.header[3]) == pv.fp_hi && pv.header[6] == pv.num_tiles;
+}
 
 // Host-side summary of a validated layout.
 struct HostLayout {
@@ -54,28 +68,32 @@ PlanView plan_view(const HostLayout &hl, const void *d_plan);
 size_t decode_workspace_bytes(const HostLayout &hl);
 
 // Launchers (return hipSuccess or the launch error).
+// Decode: `scratch` is the decode's scratch (past the workspace header), `status` the status word.
 hipError_t launch_decode(const HostLayout &hl, const PlanView &pv, const uint32_t *la,
-                         const uint32_t *ca, int32_t *row_ptr, int32_t *col_idx, void *workspace,
-                         hipStream_t stream);
+                         const uint32_t *ca, int32_t *row_ptr, int32_t *col_idx, void *scratch,
+                         int32_t *status, hipStream_t stream);
 // Fused path (no CSR): per head, the request-level CA page lists and per-row list records.
 hipError_t launch_bits_prepass(const HostLayout &hl, const PlanView &pv, const uint32_t *la, const uint32_t *ca,
                                int32_t *ca_prefix, int32_t *ca_list, int32_t *rowinfo, hipStream_t stream);
 // Offline encoder (tile masses of dense attention, then top-p selection into LA/CA words).
+// `status` (may be null): the caller's device word for the sift_device_flag bits.
 hipError_t launch_tile_masses(const HostLayout &hl, const PlanView &pv, const uint16_t *q, const uint16_t *k,
-                              float scale, float *masses, int RT, hipStream_t stream);
+                              float scale, float *masses, int RT, int32_t *status, hipStream_t stream);
 hipError_t launch_select_bits(const HostLayout &hl, const PlanView &pv, const float *masses, int RT, float p_la,
-                              float p_ca, uint32_t *la_out, uint32_t *ca_out, hipStream_t stream);
+                              float p_ca, uint32_t *la_out, uint32_t *ca_out, int32_t *status, hipStream_t stream);
 hipError_t launch_cast_bf16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);
 // V [N][Hkv][D] (bf16, or fp32 when fp32 is set) -> bf16 V^T tiles [Hkv][G][D][64] in the prefill layout;
-// also zeroes the 8 row-queue counters the attention kernel claims rows from.
-hipError_t launch_transpose_v(const HostLayout &hl, const void *v, bool fp32, uint16_t *vt, int *counters,
+// also zeroes the workspace header (the 8 row-queue counters the attention kernel claims rows
+// from, and the status word); `header` is the workspace start.
+hipError_t launch_transpose_v(const HostLayout &hl, const void *v, bool fp32, uint16_t *vt, int *header,
                               hipStream_t stream);
-// Attention over the CSR (rowinfo == nullptr) or, fused, over lists the kernel builds from the
-// pre-pass records, the CA page lists and the LA bits (row_ptr, col_idx unused).
+// Attention over the CSR (rowinfo == nullptr; col_entries readable col_idx entries) or, fused,
+// over lists the kernel builds from the pre-pass records, the CA page lists and the LA bits
+// (row_ptr, col_idx unused).  `header`: the workspace start (counters, status word).
 hipError_t launch_prefill(const HostLayout &hl, const PlanView &pv, const uint16_t *q,
                           const uint16_t *k, const uint16_t *vt, const int32_t *row_ptr,
-                          const int32_t *col_idx, const int32_t *rowinfo, const int32_t *ca_list,
-                          const uint32_t *la_bits, float scale, float *out, float *lse, int *counters,
-                          hipStream_t stream);
+                          const int32_t *col_idx, int64_t col_entries, const int32_t *rowinfo,
+                          const int32_t *ca_list, const uint32_t *la_bits, float scale, float *out, float *lse,
+                          int *header, hipStream_t stream);
 
 }  // namespace sift

@@ -59,9 +59,16 @@
  * Workspace: a call's workspace is its scratch (row-queue counters, V^T tiles,
  * decode intermediates) until its stream has passed the call.  Calls that can
  * run at the same time, e.g. on different streams, need separate workspaces;
- * calls in order on one stream may share one.
+ * calls in order on one stream may share one.  Its first 256 bytes are a
+ * header that holds, among others, the device status word of the last call
+ * that used the workspace (sift_device_status).
  * Errors: every call validates its host-side arguments first and launches
- * nothing on error.  Nothing throws across the ABI.
+ * nothing on error; that is the sift_status it returns.  What only the device
+ * can see -- a plan uploaded for another layout, a listed tile id outside
+ * [0, G), a CSR row outside the given col_idx -- the kernels report as
+ * sift_device_flag bits in a device status word, which a call clears when it
+ * starts; they never read or write out of bounds for it.  Nothing throws
+ * across the ABI.
  */
 #ifndef SIFT_H
 #define SIFT_H
@@ -81,6 +88,18 @@ typedef enum {
     SIFT_ERR_UNSUPPORTED = 3, /* valid but unsupported: head_dim not 64/128, tile not 64, int32 overflow */
     SIFT_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } sift_status;
+
+/* Bits of a device status word (see sift_device_status): what the kernels found that the host
+ * could not check.  0 = SIFT_DEVICE_OK. */
+typedef enum {
+    SIFT_DEVICE_OK = 0,
+    SIFT_DEVICE_PLAN_MISMATCH = 1, /* d_plan holds another layout's plan: the call computed nothing
+                                      (sift_decode_bits writes an empty CSR, row_ptr all 0; the
+                                      other calls leave their outputs untouched) */
+    SIFT_DEVICE_TILE_RANGE = 2,    /* a listed tile id outside [0, G): the entry was skipped */
+    SIFT_DEVICE_ROW_RANGE = 4      /* a CSR row whose [row_ptr[r], row_ptr[r+1]) is not inside
+                                      [0, col_entries]: the row was taken as empty */
+} sift_device_flag;
 
 typedef enum {
     SIFT_BF16 = 0, /* Q/K/V are bf16 */
@@ -119,8 +138,9 @@ size_t sift_workspace_bytes(const sift_layout *layout, sift_dtype dtype);
  * buffer of at least sift_plan_bytes() bytes, with one hipMemcpyAsync on
  * `stream` from a host staging copy.  A plan depends on the layout only, so one
  * upload serves every layer of a batch.  The plan carries a fingerprint of the
- * layout; decode and prefill launched with a plan of another layout do nothing
- * on the device (and the host check cannot see this), so keep them paired.
+ * layout; a kernel launched with a plan of another layout computes nothing and
+ * raises SIFT_DEVICE_PLAN_MISMATCH in the call's device status word (the host
+ * cannot see the plan's contents without a synchronisation).
  * Errors: SIFT_ERR_INVALID (layout, null), SIFT_ERR_CAPACITY (plan_bytes),
  * SIFT_ERR_HIP.
  */
@@ -134,7 +154,9 @@ sift_status sift_plan_upload(const sift_layout *layout, void *d_plan, size_t pla
  * above: d_row_ptr int32 [Hq*G + 1] and d_col_idx int32 [col_capacity].
  * col_capacity must be >= sift_csr_max_nnz(), which makes the fill safe
  * without a host read-back of nnz (nnz is row_ptr[Hq*G] on the device).
- * d_workspace: >= sift_workspace_bytes(layout, SIFT_BF16) bytes of scratch.
+ * d_workspace: >= sift_workspace_bytes(layout, SIFT_BF16) bytes of scratch; its
+ * status word gets SIFT_DEVICE_OK, or SIFT_DEVICE_PLAN_MISMATCH (and the CSR is
+ * then empty: row_ptr all 0).
  * Errors: SIFT_ERR_INVALID, SIFT_ERR_CAPACITY (col_capacity, workspace),
  * SIFT_ERR_UNSUPPORTED (nnz bound >= 2^31), SIFT_ERR_HIP.
  */
@@ -149,18 +171,22 @@ sift_status sift_decode_bits(const sift_layout *layout, const void *d_plan,
  * that, for each row (h, g), visits only the KV tiles listed in the CSR.
  * scores = scale * q.k (scale <= 0 selects 1/sqrt(head_dim)), bf16 MFMA with
  * fp32 accumulation, fp32 softmax, fp32 output d_out [N][Hq][D]; d_lse
- * [Hq][N] may be NULL.  Listed tiles outside [0, G) are skipped.
+ * [Hq][N] may be NULL.  d_col_idx holds col_entries readable int32 entries; a row
+ * whose range [row_ptr[r], row_ptr[r+1]) is not inside [0, col_entries] is taken
+ * as empty (SIFT_DEVICE_ROW_RANGE), and a listed tile outside [0, G) is skipped
+ * (SIFT_DEVICE_TILE_RANGE): no read leaves the given buffers.
  * d_q, d_k, d_v, d_out and d_workspace must be 16-byte aligned (SIFT_ERR_INVALID otherwise).
  * d_workspace: >= sift_workspace_bytes(layout, dtype) bytes of scratch; it holds
- * V transposed to bf16, tile by tile [Hkv][G][D][64] (written by the call, in a
- * token order internal to the library) and, for SIFT_FP32 inputs, the bf16 copies of Q and K.
+ * the header (status word), V transposed to bf16, tile by tile [Hkv][G][D][64]
+ * (written by the call, in a token order internal to the library) and, for
+ * SIFT_FP32 inputs, the bf16 copies of Q and K.
  * Errors: SIFT_ERR_INVALID, SIFT_ERR_CAPACITY (workspace),
  * SIFT_ERR_UNSUPPORTED (head_dim, tile), SIFT_ERR_HIP.
  */
 sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan,
                                 const void *d_q, const void *d_k, const void *d_v, sift_dtype dtype,
-                                const int32_t *d_row_ptr, const int32_t *d_col_idx, float scale,
-                                float *d_out, float *d_lse,
+                                const int32_t *d_row_ptr, const int32_t *d_col_idx, int64_t col_entries,
+                                float scale, float *d_out, float *d_lse,
                                 void *d_workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -172,7 +198,8 @@ sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan,
  * d_la, d_ca: the layer's bits as for sift_decode_bits.  Other arguments, the output and the
  * 16-byte alignment rule as for sift_sparse_prefill; the result is bit-identical to
  * sift_decode_bits followed by sift_sparse_prefill on the same bits.
- * d_workspace: >= sift_workspace_bytes(layout, dtype) bytes.
+ * d_workspace: >= sift_workspace_bytes(layout, dtype) bytes; status word as for
+ * sift_sparse_prefill.
  * Errors: SIFT_ERR_INVALID, SIFT_ERR_CAPACITY (workspace), SIFT_ERR_UNSUPPORTED (head_dim, tile,
  * a document of more than 1984 tiles), SIFT_ERR_HIP.
  */
@@ -202,13 +229,29 @@ sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_pl
  * sorted masses).  Writes every word of d_la / d_ca (layout as for sift_decode_bits).
  * Errors: SIFT_ERR_INVALID (p outside (0, 1], nulls), SIFT_ERR_CAPACITY (masses_bytes),
  * SIFT_ERR_UNSUPPORTED (a document of more than 64 tiles), SIFT_ERR_HIP.
+ *
+ * d_status (both calls, may be NULL): one device int32 that the call sets to SIFT_DEVICE_OK, or to
+ * SIFT_DEVICE_PLAN_MISMATCH when d_plan holds another layout's plan (the outputs are then left
+ * untouched).  A call with nothing to do (no tiles, no documents) leaves it as it is.
  */
 size_t sift_encode_masses_bytes(const sift_layout *layout);
 sift_status sift_tile_masses(const sift_layout *layout, const void *d_plan, const void *d_q, const void *d_k,
-                             float scale, float *d_masses, size_t masses_bytes, hipStream_t stream);
+                             float scale, float *d_masses, size_t masses_bytes, int32_t *d_status,
+                             hipStream_t stream);
 sift_status sift_select_bits(const sift_layout *layout, const void *d_plan, const float *d_masses,
                              size_t masses_bytes, float p_la, float p_ca, uint32_t *d_la, uint32_t *d_ca,
-                             hipStream_t stream);
+                             int32_t *d_status, hipStream_t stream);
+
+/*
+ * sift_device_status: enqueue on `stream` a copy of the device status word of the workspace
+ * d_workspace (>= 256 bytes) into *h_flags (host memory; a sift_device_flag bit set).  The value
+ * is that of the last call on the workspace that launched work, and is valid once the stream has
+ * passed this point (e.g. after hipStreamSynchronize).  A call with no tiles launches nothing
+ * and leaves the word as it was.
+ * Errors: SIFT_ERR_INVALID (null), SIFT_ERR_CAPACITY (workspace_bytes < 256), SIFT_ERR_HIP.
+ */
+sift_status sift_device_status(const void *d_workspace, size_t workspace_bytes, int32_t *h_flags,
+                               hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *sift_status_string(sift_status status);

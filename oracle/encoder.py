@@ -1,5 +1,8 @@
 """Oracle of the offline encoder (LA/CA bits from dense attention) -- TEST INFRASTRUCTURE.
 
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import this module;
+the product path never does, and it shares no code with the GPU library.
+
 SIFT technical summary, section 2 "Metodologia" ("Design del Sistema", the offline stage):
 each retrieved document is prefilled densely once; the positions with high attention scores
 are recorded as two bit vectors per document, layer and head -- Local-Attention (LA) bits for
@@ -15,17 +18,21 @@ the reading used here is:
     decreasing mass (ties: smaller c first), whose mass reaches p_la of the row's candidate
     mass; the diagonal tile and tile 0 are always kept;
   * CA page c of document d has the mass that the query tiles of the request's later
-    documents put on key tile c (summed over those query tiles, in increasing tile order); the
-    document keeps the smallest set of pages reaching p_ca of its total the same way; page 0 is
-    always kept.
+    documents put on key tile c; the document keeps the smallest set of pages reaching p_ca of
+    its total the same way; page 0 is always kept.
 
-tile_masses() is fp64 and is pinned by the tests (every query's probabilities sum to one, so a
-query tile's masses sum to its valid query count; brute force on tiny inputs).  select_bits()
-makes integer decisions from floating-point sums, so it runs in float32 with the kernel's
-summation order (a Hillis-Steele inclusive scan over 64 sorted slots, a sequential column sum);
-it is pinned by hand-worked cases and invariants (forced bits, reached threshold, minimality).
+Everything here is fp64 and follows that reading literally: tile_masses() evaluates the
+softmax of every request and head at once, tile_masses_by_tile() the same definition one
+query tile at a time (each query's softmax is independent of the others, so the two agree;
+the second is what the full-size checks use), select_top_p() sorts, accumulates the sorted
+masses with exactly rounded sums (math.fsum) and cuts at the first prefix that reaches
+p x total.  The pins are in the tests (probabilities of every query sum to one, uniform
+attention for Q = 0, torch's fp64 SDPA on V = identity, hand-worked selections, minimality).
 """
 from __future__ import annotations
+
+import math
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -82,7 +89,6 @@ def tile_masses(case, scale=None):
     """fp64 masses M[h, g, c] (zero outside a request's causal tile range)."""
     tile_req, _, _, req_first, _, _ = _segments(case)
     G = len(tile_req)
-    N = G * TILE
     hq, hkv, D = case.num_q_heads, case.num_kv_heads, case.head_dim
     sc = 1.0 / np.sqrt(D) if scale is None else scale
     q = _values(case, case.q)
@@ -137,60 +143,113 @@ def tile_mass_row(case, h, g, scale=None):
     return out
 
 
-def _scan64(v):
-    """Inclusive Hillis-Steele scan of 64 float32 values (each round adds the value `off` slots
-    back, all slots at once)."""
-    s = np.asarray(v, dtype=np.float32).copy()
-    off = 1
-    while off < 64:
-        prev = s.copy()
-        s[off:] = (prev[off:] + prev[:-off]).astype(np.float32)
-        off *= 2
-    return s
+def tile_masses_by_tile(case, scale=None, threads=None):
+    """fp64 masses M[h, g, c] of every row, evaluated one (query tile, KV head) at a time: the
+    queries of tile g of the q heads that read one KV head, against the keys of g's request up
+    to tile g.  The same definition as tile_masses (a per-query softmax over the valid causal
+    keys, probabilities summed over 64 x 64 tile pairs); this form needs memory for one tile's
+    scores only, and the tiles run on a thread pool (numpy releases the GIL in its kernels)."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    tile_req, _, _, req_first, _, _ = _segments(case)
+    G = len(tile_req)
+    hq, hkv, D = case.num_q_heads, case.num_kv_heads, case.head_dim
+    group = hq // hkv
+    sc = 1.0 / np.sqrt(D) if scale is None else scale
+    valid = valid_tokens(case)
+    k_all = [_values(case, case.k[:, j, :]) for j in range(hkv)]  # [N, D] per KV head
+    M = np.zeros((hq, G, G))
+
+    def one(task):
+        g, j = task
+        t0 = int(req_first[tile_req[g]])
+        s0, q0, s1 = t0 * TILE, g * TILE, (g + 1) * TILE
+        heads = range(j * group, (j + 1) * group)
+        q = np.concatenate([_values(case, case.q[q0:s1, h, :]) for h in heads])  # [group*64, D]
+        s = q @ k_all[j][s0:s1].T                                                 # [group*64, L]
+        s *= sc
+        # keys a query may not see: padded keys anywhere, and later keys of its own tile
+        s[:, ~valid[s0:s1]] = -np.inf
+        qpos = np.tile(np.arange(TILE), group)
+        s[:, q0 - s0:] = np.where(np.arange(TILE)[None, :] <= qpos[:, None], s[:, q0 - s0:], -np.inf)
+        mx = s.max(axis=1, keepdims=True)
+        mx[~np.isfinite(mx)] = 0.0
+        s -= mx
+        np.exp(s, out=s)                                       # e^(s - max), 0 for hidden keys
+        l = s.sum(axis=1)
+        nt = g + 1 - t0
+        per_tile = s.reshape(group * TILE, nt, TILE).sum(axis=2)  # [group*64, nt]: sum of e^ per key tile
+        q_ok = np.tile(valid[q0:s1], group) & (l > 0)
+        per_tile[q_ok] /= l[q_ok, None]                        # probabilities summed per key tile
+        per_tile[~q_ok] = 0.0                                  # padded queries carry no mass
+        blk = per_tile.reshape(group, TILE, nt).sum(axis=1)    # [group, nt]
+        for i, h in enumerate(heads):
+            M[h, g, t0:g + 1] = blk[i]
+
+    tasks = [(g, j) for g in range(G) for j in range(hkv)]
+    nthreads = threads or max(1, min(16, len(__import__("os").sched_getaffinity(0))))
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            with ThreadPoolExecutor(max_workers=nthreads) as ex:
+                list(ex.map(one, tasks))
+    else:  # pragma: no cover
+        with ThreadPoolExecutor(max_workers=nthreads) as ex:
+            list(ex.map(one, tasks))
+    return M
+
+
+def sorted_candidates(masses):
+    """Candidate indices by decreasing mass, ties by smaller index."""
+    m = np.asarray(masses, dtype=np.float64)
+    return sorted(range(m.size), key=lambda i: (-float(m[i]), i))
+
+
+def top_p_count(masses, p):
+    """k*: the length of the shortest prefix of the sorted candidates whose mass (an exactly
+    rounded sum) reaches p x total (total exactly rounded too); at least 1 when there is a
+    candidate.  Returns (k*, order)."""
+    m = np.asarray(masses, dtype=np.float64)
+    order = sorted_candidates(m)
+    if m.size == 0:
+        return 0, order
+    thr = float(p) * math.fsum(m.tolist())
+    vals = [float(m[i]) for i in order]
+    for k in range(1, len(vals) + 1):
+        if math.fsum(vals[:k]) >= thr:
+            return k, order
+    return len(vals), order
 
 
 def select_top_p(masses, p, forced):
-    """Indices kept from `masses` (float32, at most 64): sort by decreasing mass, ties by index;
-    keep slot i when the scanned mass before it is below p * total; then add `forced`."""
-    m = np.asarray(masses, dtype=np.float32)
-    n = m.size
-    assert n <= 64
-    order = sorted(range(n), key=lambda i: (-float(m[i]), i))
-    vals = np.zeros(64, np.float32)
-    vals[:n] = m[order]
-    s = _scan64(vals)
-    thr = np.float32(np.float32(p) * s[63])
-    keep = set()
-    for i in range(n):
-        before = np.float32(0.0) if i == 0 else s[i - 1]
-        if i == 0 or before < thr:
-            keep.add(order[i])
-    keep.update(forced)
-    return keep
+    """Indices kept from `masses`: the shortest prefix of the candidates sorted by decreasing
+    mass (ties: smaller index) that reaches p of their total, then `forced` added."""
+    k, order = top_p_count(masses, p)
+    return set(order[:k]) | set(forced)
 
 
-def ca_column_masses(case, M32):
-    """float32 CA masses per (h, doc): [sum over later-document query tiles g, in increasing g,
-    of M[h, g, first_d + c]] for c < T_d."""
+def ca_column_masses(case, M):
+    """fp64 CA masses per doc, [Hq, T_d]: page c of doc d gets sum over the query tiles g of the
+    request's later documents of M[h, g, first_d + c]."""
     tile_req, tile_doc, _, req_first, doc_first, doc_T = _segments(case)
     out = []
-    hq = case.num_q_heads
     for d in range(len(doc_T)):
         b = tile_req[doc_first[d]]
         later = [g for g in range(len(tile_req)) if tile_req[g] == b and tile_doc[g] > d]
-        cm = np.zeros((hq, doc_T[d]), np.float32)
-        for g in later:
-            cm = (cm + M32[:, g, doc_first[d]:doc_first[d] + doc_T[d]]).astype(np.float32)
+        cols = slice(doc_first[d], doc_first[d] + doc_T[d])
+        cm = np.asarray(M, dtype=np.float64)[:, later, cols].sum(axis=1) if later else \
+            np.zeros((case.num_q_heads, doc_T[d]))
         out.append(cm)
     return out
 
 
 def select_bits(case, M, p_la=0.9, p_ca=0.9):
-    """LA / CA booleans (lists per doc of [Hq, T, T] and [Hq, T]) from masses M (used as float32)."""
-    M32 = np.asarray(M, dtype=np.float32)
+    """LA / CA booleans (lists per doc of [Hq, T, T] and [Hq, T]) from fp64 masses M."""
+    M = np.asarray(M, dtype=np.float64)
     _, _, _, _, doc_first, doc_T = _segments(case)
     hq = case.num_q_heads
-    cms = ca_column_masses(case, M32)
+    cms = ca_column_masses(case, M)
     la, ca = [], []
     for d in range(len(doc_T)):
         T, t0 = int(doc_T[d]), int(doc_first[d])
@@ -198,7 +257,7 @@ def select_bits(case, M, p_la=0.9, p_ca=0.9):
         ca_d = np.zeros((hq, T), bool)
         for h in range(hq):
             for r in range(T):
-                keep = select_top_p(M32[h, t0 + r, t0:t0 + r + 1], p_la, {0, r})
+                keep = select_top_p(M[h, t0 + r, t0:t0 + r + 1], p_la, {0, r})
                 la_d[h, r, sorted(keep)] = True
             keep = select_top_p(cms[d][h], p_ca, {0})
             ca_d[h, sorted(keep)] = True

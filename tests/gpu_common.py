@@ -22,6 +22,15 @@ def config(cid):
     return W.config_case(cid)
 
 
+@functools.lru_cache(maxsize=1)
+def oracle_full(cid):
+    """The fp64 oracle's whole output (O [N, Hq, D], LSE [Hq, N]) of a workload, kept for the
+    next test that asks for the same workload."""
+    import oracle
+    print(f"oracle: workload {cid}, every (token, head)", flush=True)
+    return oracle.attention(config(cid))
+
+
 def words_tensor(words):
     w = np.ascontiguousarray(words, dtype=np.uint32)
     if w.size == 0:
@@ -75,6 +84,21 @@ def valid_tokens(case):
         t = -(-m // 64)
         valid.extend([x < m for x in range(64 * t)])
     return np.array(valid, dtype=bool)
+
+
+def assert_full_parity(case, out, lse, ref, ref_lse, what):
+    """Every valid (token, head) output and LSE against the oracle; padded query rows exactly 0
+    with LSE -inf."""
+    valid = valid_tokens(case)
+    mx, mean = assert_close(out[valid], ref[valid], what)
+    assert np.all(out[~valid] == 0.0), f"{what}: padded query rows must be exactly 0"
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(lse)), f"{what}: LSE finiteness differs"
+    lmx = float(np.max(np.abs(lse[fin] - ref_lse[fin]), initial=0.0))
+    assert lmx <= LSE_ABS, f"{what}: LSE max_abs {lmx:.3e}"
+    print(f"{what}: {int(valid.sum()) * case.num_q_heads} (token, head) outputs, max_abs {mx:.3e} "
+          f"mean_abs {mean:.3e}, LSE max_abs {lmx:.3e}", flush=True)
+    return mx, mean
 
 
 def assert_close(got, ref, what=""):

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTED) == declared
-    assert lib.sift_abi_version() >> 16 == 1
+    assert lib.sift_abi_version() >> 16 == 2
 
 
 @pytest.mark.parametrize("cid", [1, 2])
@@ -106,23 +106,30 @@ def test_prefill_validation_rejects_before_any_launch():
     lay = sift.Layout.from_case(case)
     lib = sift.library()
     vp = ctypes.c_void_p
-    st = lib.sift_sparse_prefill(lay.ref, vp(1), vp(0), vp(1), vp(1), B.SIFT_BF16, vp(1), vp(1),
+    st = lib.sift_sparse_prefill(lay.ref, vp(1), vp(0), vp(1), vp(1), B.SIFT_BF16, vp(1), vp(1), 10,
                                  ctypes.c_float(0.0), vp(1), vp(0), vp(0), 0, vp(0))
     assert st == B.SIFT_ERR_INVALID
-    st = lib.sift_sparse_prefill(lay.ref, vp(1), vp(1), vp(1), vp(1), 7, vp(1), vp(1),
+    st = lib.sift_sparse_prefill(lay.ref, vp(1), vp(1), vp(1), vp(1), 7, vp(1), vp(1), 10,
                                  ctypes.c_float(0.0), vp(1), vp(0), vp(0), 0, vp(0))
     assert st == B.SIFT_ERR_INVALID
     # Q/K/V/O must be 16-byte aligned (fake, never dereferenced, addresses)
     a = vp(4096)
-    st = lib.sift_sparse_prefill(lay.ref, a, vp(4096 + 8), a, a, B.SIFT_BF16, a, a,
+    st = lib.sift_sparse_prefill(lay.ref, a, vp(4096 + 8), a, a, B.SIFT_BF16, a, a, 10,
                                  ctypes.c_float(0.0), a, vp(0), a, 1 << 30, vp(0))
     assert st == B.SIFT_ERR_INVALID
-    # the workspace holds V^T (bf16), plus the bf16 copies of Q and K for fp32 inputs
+    # col_entries: not negative, and col_idx may be null only when it is 0
+    st = lib.sift_sparse_prefill(lay.ref, a, a, a, a, B.SIFT_BF16, a, a, -1,
+                                 ctypes.c_float(0.0), a, vp(0), a, 1 << 30, vp(0))
+    assert st == B.SIFT_ERR_INVALID
+    st = lib.sift_sparse_prefill(lay.ref, a, a, a, a, B.SIFT_BF16, a, vp(0), 5,
+                                 ctypes.c_float(0.0), a, vp(0), a, 1 << 30, vp(0))
+    assert st == B.SIFT_ERR_INVALID
+    # the workspace holds the header and V^T (bf16), plus the bf16 copies of Q and K for fp32 inputs
     for dt in (B.SIFT_BF16, B.SIFT_FP32):
-        st = lib.sift_sparse_prefill(lay.ref, a, a, a, a, dt, a, a,
+        st = lib.sift_sparse_prefill(lay.ref, a, a, a, a, dt, a, a, 10,
                                      ctypes.c_float(0.0), a, vp(0), vp(0), 0, vp(0))
         assert st == B.SIFT_ERR_CAPACITY
-    vt = 2 * lay.padded_tokens * lay.num_kv_heads * lay.head_dim
+    vt = 256 + 2 * lay.padded_tokens * lay.num_kv_heads * lay.head_dim
     assert lay.workspace_bytes(B.SIFT_BF16) >= vt
     assert lay.workspace_bytes(B.SIFT_FP32) >= vt + 2 * lay.padded_tokens * (lay.num_q_heads + lay.num_kv_heads) * lay.head_dim
 
@@ -190,12 +197,73 @@ def test_encoder_validation():
         rt = max(rt, sum(tiles[d0:d0 + k]) + -(-int(case.question_len[b]) // 64))
         d0 += k
     assert need == 4 * lay.num_q_heads * lay.num_tiles * rt
-    assert lib.sift_tile_masses(lay.ref, a, vp(0), a, f(0.0), a, need, vp(0)) == B.SIFT_ERR_INVALID
-    assert lib.sift_tile_masses(lay.ref, a, vp(4104), a, f(0.0), a, need, vp(0)) == B.SIFT_ERR_INVALID
-    assert lib.sift_tile_masses(lay.ref, a, a, a, f(0.0), a, need - 4, vp(0)) == B.SIFT_ERR_CAPACITY
+    assert lib.sift_tile_masses(lay.ref, a, vp(0), a, f(0.0), a, need, vp(0), vp(0)) == B.SIFT_ERR_INVALID
+    assert lib.sift_tile_masses(lay.ref, a, vp(4104), a, f(0.0), a, need, vp(0), vp(0)) == B.SIFT_ERR_INVALID
+    assert lib.sift_tile_masses(lay.ref, a, a, a, f(0.0), a, need - 4, vp(0), vp(0)) == B.SIFT_ERR_CAPACITY
     for p_la, p_ca in ((0.0, 0.5), (0.5, 1.5), (float("nan"), 0.5)):
-        assert lib.sift_select_bits(lay.ref, a, a, need, f(p_la), f(p_ca), a, a, vp(0)) == B.SIFT_ERR_INVALID
-    assert lib.sift_select_bits(lay.ref, a, a, need - 4, f(0.9), f(0.9), a, a, vp(0)) == B.SIFT_ERR_CAPACITY
+        assert lib.sift_select_bits(lay.ref, a, a, need, f(p_la), f(p_ca), a, a, vp(0), vp(0)) == B.SIFT_ERR_INVALID
+    assert lib.sift_select_bits(lay.ref, a, a, need - 4, f(0.9), f(0.9), a, a, vp(0), vp(0)) == B.SIFT_ERR_CAPACITY
     big = sift.Layout([1], [65 * 64], [0], 1, 1, 64)
     nb = lib.sift_encode_masses_bytes(big.ref)
-    assert lib.sift_select_bits(big.ref, a, a, nb, f(0.9), f(0.9), a, a, vp(0)) == B.SIFT_ERR_UNSUPPORTED
+    assert lib.sift_select_bits(big.ref, a, a, nb, f(0.9), f(0.9), a, a, vp(0), vp(0)) == B.SIFT_ERR_UNSUPPORTED
+
+
+def test_device_status_validation():
+    lib = sift.library()
+    vp = ctypes.c_void_p
+    flags = ctypes.c_int32(-1)
+    assert lib.sift_device_status(vp(0), 4096, ctypes.addressof(flags), vp(0)) == B.SIFT_ERR_INVALID
+    assert lib.sift_device_status(vp(4096), 4096, vp(0), vp(0)) == B.SIFT_ERR_INVALID
+    assert lib.sift_device_status(vp(4096), 255, ctypes.addressof(flags), vp(0)) == B.SIFT_ERR_CAPACITY
+    assert flags.value == -1  # nothing enqueued
+
+
+def _cpu_inputs(case, torch):
+    q = torch.from_numpy(case.q.view(np.int16)).view(torch.bfloat16)
+    k = torch.from_numpy(case.k.view(np.int16)).view(torch.bfloat16)
+    v = torch.from_numpy(case.v.view(np.int16)).view(torch.bfloat16)
+    return q, k, v
+
+
+def test_binding_rejects_bad_output_and_csr_tensors():
+    """The binding checks every caller-supplied tensor (shape, dtype, device, contiguity) before
+    the C call: the C ABI cannot know their sizes, and a short buffer would be an out-of-bounds
+    device write.  (CPU tensors here: the checks raise before any device work.)"""
+    import torch
+    case = W.random_small_case(6, d=64, hq=2, hkv=1)
+    lay = sift.Layout.from_case(case)
+    q, k, v = _cpu_inputs(case, torch)
+    n, hq, d = lay.padded_tokens, lay.num_q_heads, lay.head_dim
+    rp = torch.zeros(lay.num_rows + 1, dtype=torch.int32)
+    ci = torch.zeros(max(lay.csr_max_nnz, 1), dtype=torch.int32)
+    good_out = torch.empty((n, hq, d), dtype=torch.float32)
+    bad = [
+        dict(out=torch.empty((n, hq, d), dtype=torch.bfloat16)),
+        dict(out=torch.empty((n - 1, hq, d), dtype=torch.float32)),
+        dict(out=torch.empty((n, d, hq), dtype=torch.float32).transpose(1, 2)),
+        dict(out=good_out, want_lse=True, lse=torch.empty((n, hq), dtype=torch.float32)),
+        dict(out=good_out, want_lse=True, lse=torch.empty((hq, n), dtype=torch.float64)),
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            sift.sparse_prefill(lay, q, k, v, rp, ci, **kw)
+    with pytest.raises(ValueError):
+        sift.sparse_prefill(lay, q, k, v, rp[:-1], ci, out=good_out)
+    with pytest.raises(ValueError):
+        sift.sparse_prefill(lay, q, k, v, rp.to(torch.int64), ci, out=good_out)
+    with pytest.raises(ValueError):
+        sift.sparse_prefill(lay, q, k, v, rp, ci.to(torch.int64), out=good_out)
+    with pytest.raises(ValueError):
+        sift.sparse_prefill(lay, q, k, v, rp, ci[::2], out=good_out)
+    la = torch.from_numpy(case.la_words.view(np.int32))
+    ca = torch.from_numpy(case.ca_words.view(np.int32))
+    with pytest.raises(ValueError):
+        sift.decode_bits(lay, la, ca, row_ptr=torch.zeros(lay.num_rows, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        sift.decode_bits(lay, la, ca, row_ptr=rp, col_idx=torch.zeros(lay.csr_max_nnz - 1, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        sift.sparse_prefill_bits(lay, la, ca, q, k, v, out=torch.empty((n, hq, d - 1), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        sift.tile_masses(lay, q, k, masses=torch.empty(3, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        sift.tile_masses(lay, q, k, status=torch.empty(1, dtype=torch.int64))

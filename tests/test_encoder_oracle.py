@@ -1,5 +1,8 @@
 """Pins of the encoder oracle (oracle/encoder.py): closed forms, special cases, hand-worked
 selections and invariants."""
+import itertools
+import math
+
 import numpy as np
 import pytest
 
@@ -70,18 +73,48 @@ def test_select_top_p_hand_worked(masses, p, forced, want):
 def test_select_top_p_is_the_minimal_sorted_prefix(seed):
     rng = np.random.default_rng(seed)
     n = int(rng.integers(1, 65))
-    m = rng.random(n).astype(np.float32) ** 3
+    m = rng.random(n) ** 3
     p = float(rng.uniform(0.1, 1.0))
     keep = E.select_top_p(m, p, set())
     order = sorted(range(n), key=lambda i: (-float(m[i]), i))
     k = len(keep)
     assert keep == set(order[:k])
-    tot = float(m.astype(np.float64).sum())
-    kept = float(m[order[:k]].astype(np.float64).sum())
-    # reaches the threshold (float32 scan: allow one rounding), and one fewer does not
-    assert kept >= p * tot * (1 - 1e-5) or k == n
+    tot = math.fsum(m.tolist())
+    # reaches the threshold, and one fewer does not (exactly rounded sums)
+    assert math.fsum(m[order[:k]].tolist()) >= p * tot
     if k > 1:
-        assert float(m[order[:k - 1]].astype(np.float64).sum()) < p * tot * (1 + 1e-5)
+        assert math.fsum(m[order[:k - 1]].tolist()) < p * tot
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_select_top_p_brute_force_over_all_subsets(seed):
+    """Brute force over every subset of up to 10 candidates: the size of the kept set is the
+    smallest size of any subset whose mass reaches p x total, and among the subsets of that
+    size the kept one has the largest mass (ties: the smaller indices).  Masses are multiples of
+    1/8 half of the time, so exact ties and exact hits of the threshold occur."""
+    rng = np.random.default_rng(500 + seed)
+    n = int(rng.integers(1, 11))
+    m = rng.integers(0, 6, size=n) / 8.0 if seed % 2 else rng.random(n)
+    p = [0.25, 0.5, 0.75, 1.0, float(rng.uniform(0.05, 1.0))][seed % 5]
+    tot = math.fsum(m.tolist())
+    best = None
+    for size in range(1, n + 1):
+        reach = [s for s in itertools.combinations(range(n), size) if math.fsum(m[list(s)].tolist()) >= p * tot]
+        if reach:
+            top = max(math.fsum(m[list(s)].tolist()) for s in reach)
+            cands = [s for s in reach if math.fsum(m[list(s)].tolist()) == top]
+            # among equal masses the tie order prefers smaller indices: the lexicographically
+            # smallest sorted-index tuple of the top subsets that is also a top-by-mass prefix
+            best = (size, cands)
+            break
+    keep = E.select_top_p(m, p, set())
+    assert best is not None and len(keep) == best[0]
+    assert any(set(c) == keep for c in best[1])
+    # every kept mass is >= every dropped mass; equal masses are kept smaller index first
+    drop = set(range(n)) - keep
+    for i in keep:
+        for j in drop:
+            assert m[i] > m[j] or (m[i] == m[j] and i < j)
 
 
 def test_select_bits_forced_and_last_document():
@@ -168,3 +201,11 @@ def test_select_bits_hand_worked():
     np.testing.assert_array_equal(la[1][0], want_la1)
     np.testing.assert_array_equal(ca[0][0], [True, False, True])
     np.testing.assert_array_equal(ca[1][0], [True, False])
+
+
+@pytest.mark.parametrize("seed,hq,hkv", [(60, 4, 2), (61, 3, 1), (62, 2, 2), (63, 8, 2)])
+def test_masses_by_tile_equal_the_whole_request_evaluation(seed, hq, hkv):
+    """The per-(query tile, KV head) evaluation used at full size gives the whole-request
+    matrices (ragged documents and questions, padded queries and keys, GQA)."""
+    case = W.random_small_case(seed, max_requests=2, max_docs=3, max_tiles=4, hq=hq, hkv=hkv, d=16)
+    np.testing.assert_allclose(E.tile_masses_by_tile(case, threads=3), E.tile_masses(case), rtol=0, atol=1e-12)

@@ -7,8 +7,8 @@ import torch
 import oracle
 import bit_vector_block_amd as sift
 from bit_vector_block_amd import workloads as W
-from gpu_common import (DEV, assert_close, config, gpu_prefill, valid_tokens, values_tensor,
-                        words_tensor)
+from gpu_common import (DEV, assert_close, assert_full_parity, config, gpu_prefill, oracle_full,
+                        valid_tokens, values_tensor, words_tensor)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +45,15 @@ def test_fused_random_small(seed):
 @pytest.mark.parametrize("cid", [2, 3, 4, 5])
 def test_fused_configs_same_as_csr(cid):
     _same_as_csr_path(config(cid))
+
+
+def test_fused_config2_every_element_against_the_oracle():
+    """The fused call on workload 2 against the fp64 oracle directly (every valid output and
+    LSE), not only against the CSR path."""
+    case = config(2)
+    out, lse = fused_prefill(case)
+    ref, ref_lse = oracle_full(2)
+    assert_full_parity(case, out, lse, ref, ref_lse, "fused, config 2")
 
 
 def test_fused_long_documents_multiword_rows():

@@ -7,7 +7,8 @@ import pytest
 import oracle
 from bit_vector_block_amd import workloads as W
 import bit_vector_block_amd as sift
-from gpu_common import LSE_ABS, assert_close, config, gpu_decode, gpu_prefill, valid_tokens
+from gpu_common import (LSE_ABS, assert_close, assert_full_parity, config, gpu_decode, gpu_prefill,
+                        oracle_full, valid_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -142,43 +143,92 @@ def _sample_pairs(case, rng, n_random):
     return heads.astype(np.int32), toks.astype(np.int64)
 
 
-@pytest.mark.parametrize("cid,n_random", [(2, 3000), (3, 1500), (4, 1000), (5, 600)])
-def test_prefill_configs_sampled(cid, n_random):
+@pytest.mark.parametrize("cid", [2, 3, 4])
+def test_prefill_configs_every_element(cid):
+    """Workloads 2-4 at full size: every valid (token, head) output and every LSE against the
+    fp64 oracle; padded query rows exactly 0."""
     case = config(cid)
     print(f"prefill config {cid}: N={case.q.shape[0]} Hq={case.num_q_heads}", flush=True)
+    out, lse = gpu_prefill(case)
+    ref, ref_lse = oracle_full(cid)
+    assert_full_parity(case, out, lse, ref, ref_lse, f"config {cid}")
+
+
+def _stratified_rows(case, rp, frac, rng):
+    """CSR rows (h, g) of workload 5: in every head, a fraction `frac` of the rows drawn in each
+    tenth of the head's row-length order (so short, medium and long rows all appear), plus the
+    last question tile of every request in every head (the longest rows)."""
+    hq = case.num_q_heads
+    G = (len(rp) - 1) // hq
+    lengths = np.diff(rp).reshape(hq, G)
+    from oracle import encoder as E  # segment tables only
+    tile_req, tile_doc, _, _, _, _ = E._segments(case)
+    last_q = [g for g in range(G) if tile_doc[g] < 0 and (g + 1 == G or tile_req[g + 1] != tile_req[g])]
+    rows = set()
+    for h in range(hq):
+        order = np.argsort(lengths[h], kind="stable")
+        for part in np.array_split(order, 10):
+            k = max(1, int(np.ceil(frac * part.size)))
+            rows.update((h, int(g)) for g in rng.choice(part, size=k, replace=False))
+        rows.update((h, g) for g in last_q)
+    return sorted(rows), lengths
+
+
+def test_prefill_config5_stratified_whole_rows():
+    """The ragged batch (4 requests, Beta(2, 8) per-head densities): whole CSR rows (all 64
+    queries of a (head, query tile)) for at least 5 % of the rows of every head, stratified by row
+    length, and the longest question rows of every request and head."""
+    case = config(5)
+    print(f"prefill config 5: N={case.q.shape[0]} Hq={case.num_q_heads}", flush=True)
     out, lse = gpu_prefill(case)
     valid = valid_tokens(case)
     assert np.all(np.isfinite(out)), "non-finite output"
     assert np.all(out[~valid] == 0.0), "padded query rows must be exactly 0"
-    rng = np.random.default_rng(cid)
-    heads, toks = _sample_pairs(case, rng, n_random)
+    rp, _ = oracle.decode(case)
+    rows, lengths = _stratified_rows(case, rp, 0.05, np.random.default_rng(55))
+    assert len(rows) >= 0.05 * lengths.size
+    heads = np.repeat(np.array([h for h, _ in rows], np.int32), 64)
+    toks = (np.array([g for _, g in rows], np.int64)[:, None] * 64 + np.arange(64)).ravel()
+    picked = np.array([lengths[h, g] for h, g in rows])
+    print(f"config 5: {len(rows)} of {lengths.size} rows, lengths {picked.min()}..{picked.max()} "
+          f"(all rows {lengths.min()}..{lengths.max()})", flush=True)
+    assert picked.max() == lengths.max()
     ref, ref_lse = oracle.attention(case, heads=heads, tokens=toks)
-    got = out[toks, heads]
     keep = valid[toks]
-    mx, mean = assert_close(got[keep], ref[keep], f"config {cid}")
+    mx, mean = assert_close(out[toks, heads][keep], ref[keep], "config 5 rows")
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(lse[heads, toks]))
+    assert np.max(np.abs(lse[heads, toks][fin] - ref_lse[fin]), initial=0.0) <= LSE_ABS
+    print(f"config 5: {int(keep.sum())} (token, head) outputs, max_abs {mx:.3e} mean_abs {mean:.3e}")
+
+
+def test_prefill_config5_sampled_pairs():
+    """Extra check of workload 5 on random (head, token) pairs all over the batch."""
+    case = config(5)
+    out, lse = gpu_prefill(case)
+    valid = valid_tokens(case)
+    rng = np.random.default_rng(5)
+    heads, toks = _sample_pairs(case, rng, 600)
+    ref, ref_lse = oracle.attention(case, heads=heads, tokens=toks)
+    keep = valid[toks]
+    assert_close(out[toks, heads][keep], ref[keep], "config 5 pairs")
     fin = np.isfinite(ref_lse)
     assert np.max(np.abs(lse[heads, toks][fin] - ref_lse[fin]), initial=0.0) <= LSE_ABS
-    print(f"config {cid}: {keep.sum()} sampled rows, max_abs {mx:.3e} mean_abs {mean:.3e}")
 
 
-def test_prefill_full_recompute_config2_sampled():
+def test_prefill_full_recompute_config2_every_element():
     """Full recompute (every LA and CA bit set, i.e. dense causal attention per request) at the
-    10 x 1k-token, 32/8-head, d=128 size, through the same decode and prefill launches."""
+    10 x 1k-token, 32/8-head, d=128 size, through the same decode and prefill launches: every
+    valid output against the oracle."""
     case = config(2)
     case = W.with_bits(case, *W.all_ones_bits(case))
     rp, ci = gpu_decode(case)
     lay = sift.Layout.from_case(case)
     assert rp[-1] == lay.csr_max_nnz, "all-ones bits must give the dense causal tile count"
     out, lse = gpu_prefill(case)
-    valid = valid_tokens(case)
-    rng = np.random.default_rng(22)
-    heads, toks = _sample_pairs(case, rng, 1500)
-    ref, ref_lse = oracle.attention(case, heads=heads, tokens=toks)
-    keep = valid[toks]
-    mx, mean = assert_close(out[toks, heads][keep], ref[keep], "full recompute, config 2")
-    fin = np.isfinite(ref_lse)
-    assert np.max(np.abs(lse[heads, toks][fin] - ref_lse[fin]), initial=0.0) <= LSE_ABS
-    print(f"full recompute: {keep.sum()} sampled rows, max_abs {mx:.3e} mean_abs {mean:.3e}")
+    print("oracle: full recompute of workload 2", flush=True)
+    ref, ref_lse = oracle.attention(case)
+    assert_full_parity(case, out, lse, ref, ref_lse, "full recompute, config 2")
 
 
 def test_prefill_single_key_is_exact():
