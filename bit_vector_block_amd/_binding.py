@@ -20,13 +20,15 @@ SIFT_OK, SIFT_ERR_INVALID, SIFT_ERR_CAPACITY, SIFT_ERR_UNSUPPORTED, SIFT_ERR_HIP
 SIFT_BF16, SIFT_FP32 = 0, 1
 # bits of a device status word (sift_device_flag)
 SIFT_DEVICE_OK, SIFT_DEVICE_PLAN_MISMATCH, SIFT_DEVICE_TILE_RANGE, SIFT_DEVICE_ROW_RANGE = 0, 1, 2, 4
+# scratch array of sift_decode_bits_noalloc, per GPU (SIFT_DECODE_NOALLOC_MAX_BYTES)
+DECODE_NOALLOC_MAX_BYTES = 8 << 20
 
 EXPORTED = (
     "sift_num_tiles", "sift_padded_tokens", "sift_num_rows", "sift_la_words", "sift_ca_words",
     "sift_csr_max_nnz", "sift_plan_bytes", "sift_workspace_bytes", "sift_plan_upload",
     "sift_decode_bits", "sift_sparse_prefill", "sift_sparse_prefill_bits", "sift_status_string",
     "sift_abi_version", "sift_encode_masses_bytes", "sift_tile_masses", "sift_select_bits",
-    "sift_device_status",
+    "sift_device_status", "sift_decode_bits_noalloc",
 )
 
 
@@ -87,6 +89,8 @@ def _lib():
     lib.sift_select_bits.restype = ctypes.c_int
     lib.sift_device_status.argtypes = [vp, sz, vp, vp]
     lib.sift_device_status.restype = ctypes.c_int
+    lib.sift_decode_bits_noalloc.argtypes = [L, vp, vp, vp, vp, vp, i64, vp]
+    lib.sift_decode_bits_noalloc.restype = ctypes.c_int
     lib.sift_status_string.argtypes = [ctypes.c_int]
     lib.sift_status_string.restype = ctypes.c_char_p
     lib.sift_abi_version.argtypes = []
@@ -245,6 +249,26 @@ def decode_bits(layout: Layout, la, ca, plan=None, workspace=None, row_ptr=None,
         ctypes.c_void_p(ca.data_ptr()), ctypes.c_void_p(row_ptr.data_ptr()),
         ctypes.c_void_p(col_idx.data_ptr()), col_idx.numel(), ctypes.c_void_p(ws.data_ptr()),
         ws_bytes, _stream_handle(torch, device)), "sift_decode_bits")
+    return row_ptr, col_idx
+
+
+def decode_bits_noalloc(layout: Layout, la, ca, plan, row_ptr, col_idx):
+    """decode_bits without a workspace: the library's own per-GPU scratch array (see
+    sift_decode_bits_noalloc).  The caller passes every buffer (plan, row_ptr int32 [Hq*G+1],
+    col_idx int32 [>= csr_max_nnz]); nothing is allocated.  Calls on one GPU must not overlap."""
+    import torch
+    device = la.device
+    for name, t, n in (("la", la, layout.la_words), ("ca", ca, layout.ca_words)):
+        if t.device != device or not t.is_contiguous() or t.element_size() != 4 or t.numel() < n:
+            raise ValueError(f"{name}: need a contiguous 32-bit device tensor of >= {n} words")
+    _need_tensor("row_ptr", row_ptr, torch.int32, device, shape=(layout.num_rows + 1,))
+    _need_tensor("col_idx", col_idx, torch.int32, device, min_numel=layout.csr_max_nnz)
+    _need_tensor("plan", plan, torch.uint8, device, min_numel=layout.plan_bytes)
+    _check(_lib().sift_decode_bits_noalloc(
+        layout.ref, ctypes.c_void_p(plan.data_ptr()), ctypes.c_void_p(la.data_ptr()),
+        ctypes.c_void_p(ca.data_ptr()), ctypes.c_void_p(row_ptr.data_ptr()),
+        ctypes.c_void_p(col_idx.data_ptr()), col_idx.numel(), _stream_handle(torch, device)),
+        "sift_decode_bits_noalloc")
     return row_ptr, col_idx
 
 

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "sift_internal.hpp"
 
@@ -205,6 +206,39 @@ static size_t bits_tables_bytes(const HostLayout &hl) {
            align256(32 * rows);
 }
 
+// Scratch of the allocation-free decode (sift_decode_bits_noalloc): one array per GPU, in the
+// library's code object, held until the process ends.  Host code never passes its name to a
+// kernel -- that would be a host-side stand-in -- but the per-device address that
+// hipGetSymbolAddress returns, looked up once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = SIFT_DECODE_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device of `stream`, which must be the current device.
+sift_status noalloc_scratch(hipStream_t stream, char **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SIFT_ERR_HIP;
+    if (stream != nullptr) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return SIFT_ERR_HIP;
+        if (sdev != dev) return SIFT_ERR_INVALID;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return SIFT_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SIFT_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<char *>(g_scratch_ptr[dev]);
+    return SIFT_OK;
+}
+}  // namespace
+
 }  // namespace sift
 
 using namespace sift;
@@ -295,6 +329,27 @@ sift_status sift_decode_bits(const sift_layout *layout, const void *d_plan, cons
     if (!d_workspace || workspace_bytes < decode_workspace_bytes(hl)) return SIFT_ERR_CAPACITY;
     const PlanView pv = plan_view(hl, d_plan);
     char *ws = static_cast<char *>(d_workspace);
+    if (launch_decode(hl, pv, d_la, d_ca, d_row_ptr, d_col_idx, ws + kWorkspaceHeader,
+                      reinterpret_cast<int32_t *>(ws) + kStatusWord, stream) != hipSuccess)
+        return SIFT_ERR_HIP;
+    return SIFT_OK;
+}
+
+sift_status sift_decode_bits_noalloc(const sift_layout *layout, const void *d_plan, const uint32_t *d_la,
+                                     const uint32_t *d_ca, int32_t *d_row_ptr, int32_t *d_col_idx,
+                                     int64_t col_capacity, hipStream_t stream) {
+    HostLayout hl;
+    sift_status st = build_layout(layout, &hl);
+    if (st != SIFT_OK) return st;
+    if (!d_plan || !d_row_ptr) return SIFT_ERR_INVALID;
+    if ((hl.la_words > 0 && !d_la) || (hl.ca_words > 0 && !d_ca)) return SIFT_ERR_INVALID;
+    if (hl.max_nnz > 0 && !d_col_idx) return SIFT_ERR_INVALID;
+    if (col_capacity < hl.max_nnz) return SIFT_ERR_CAPACITY;
+    if (decode_workspace_bytes(hl) > kNoAllocScratchBytes) return SIFT_ERR_CAPACITY;
+    char *ws = nullptr;
+    st = noalloc_scratch(stream, &ws);
+    if (st != SIFT_OK) return st;
+    const PlanView pv = plan_view(hl, d_plan);
     if (launch_decode(hl, pv, d_la, d_ca, d_row_ptr, d_col_idx, ws + kWorkspaceHeader,
                       reinterpret_cast<int32_t *>(ws) + kStatusWord, stream) != hipSuccess)
         return SIFT_ERR_HIP;

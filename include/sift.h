@@ -89,6 +89,9 @@ typedef enum {
     SIFT_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } sift_status;
 
+/* Bytes of the per-GPU scratch array of sift_decode_bits_noalloc. */
+#define SIFT_DECODE_NOALLOC_MAX_BYTES ((size_t)8 << 20)
+
 /* Bits of a device status word (see sift_device_status): what the kernels found that the host
  * could not check.  0 = SIFT_DEVICE_OK. */
 typedef enum {
@@ -164,6 +167,22 @@ sift_status sift_decode_bits(const sift_layout *layout, const void *d_plan,
                              const uint32_t *d_la, const uint32_t *d_ca,
                              int32_t *d_row_ptr, int32_t *d_col_idx, int64_t col_capacity,
                              void *d_workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sift_decode_bits_noalloc: sift_decode_bits for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument and no allocation.  The decode's scratch is an array of the library's own,
+ * one per GPU, of SIFT_DECODE_NOALLOC_MAX_BYTES bytes (8 MiB), held until the process ends;
+ * layouts whose decode scratch is larger (sift_workspace_bytes, about 8 Hq G bytes plus
+ * 4 Hq ndocs) get SIFT_ERR_CAPACITY.  `stream` must belong to the current device.  Same
+ * arguments, output and errors as sift_decode_bits otherwise; a plan of another layout gives an
+ * empty CSR (row_ptr all 0).  Every call on a GPU shares that GPU's array: calls that can run at
+ * the same time on one GPU (other streams, other threads) race and must not overlap.
+ */
+sift_status sift_decode_bits_noalloc(const sift_layout *layout, const void *d_plan,
+                                     const uint32_t *d_la, const uint32_t *d_ca,
+                                     int32_t *d_row_ptr, int32_t *d_col_idx, int64_t col_capacity,
+                                     hipStream_t stream);
 
 /*
  * sift_sparse_prefill: the sparse attention kernel of "Dettagli di

@@ -267,3 +267,21 @@ def test_binding_rejects_bad_output_and_csr_tensors():
         sift.tile_masses(lay, q, k, masses=torch.empty(3, dtype=torch.float32))
     with pytest.raises(ValueError):
         sift.tile_masses(lay, q, k, status=torch.empty(1, dtype=torch.int64))
+
+
+def test_noalloc_decode_rejects_a_layout_beyond_its_scratch():
+    """The allocation-free decode's scratch is a fixed array per GPU: a layout whose decode
+    scratch is larger (200 requests x 100 tiles, 64 q heads: about 10 MiB) is rejected on the
+    host, before any HIP call (fake, never dereferenced, pointers)."""
+    lib = sift.library()
+    lay = sift.Layout([1] * 200, [6400] * 200, [0] * 200, 64, 8, 128)
+    scratch = 256 + 4 * 64 * 200 + 2 * 4 * 64 * lay.num_tiles
+    assert lay.num_tiles == 20000 and scratch > B.DECODE_NOALLOC_MAX_BYTES
+    a = ctypes.c_void_p(4096)
+    st = lib.sift_decode_bits_noalloc(lay.ref, a, a, a, a, a, lay.csr_max_nnz, ctypes.c_void_p(0))
+    assert st == B.SIFT_ERR_CAPACITY
+    small = sift.Layout([1], [640], [0], 2, 1, 64)
+    assert lib.sift_decode_bits_noalloc(small.ref, a, a, a, a, a, small.csr_max_nnz - 1,
+                                        ctypes.c_void_p(0)) == B.SIFT_ERR_CAPACITY
+    assert lib.sift_decode_bits_noalloc(small.ref, ctypes.c_void_p(0), a, a, a, a, small.csr_max_nnz,
+                                        ctypes.c_void_p(0)) == B.SIFT_ERR_INVALID
