@@ -14,11 +14,10 @@ workloads in ``workloads`` and the multi-layer stream orchestration in ``pipelin
 """
 from ._binding import (SIFT_BF16, SIFT_DEVICE_OK, SIFT_DEVICE_PLAN_MISMATCH, SIFT_DEVICE_ROW_RANGE,
                        SIFT_DEVICE_TILE_RANGE, SIFT_FP32, Layout, SiftError, decode_bits, decode_bits_noalloc,
-                       default_scale,
-                       device_status, encode_masses_bytes, library, plan_upload, select_bits, sparse_prefill,
-                       sparse_prefill_bits, tile_masses, workspace)
+                       default_scale, device_status, encode_masses_bytes, encode_workspace_bytes, library,
+                       plan_upload, select_bits, sparse_prefill, sparse_prefill_bits, tile_masses, workspace)
 
-__all__ = ["Layout", "SiftError", "decode_bits", "decode_bits_noalloc", "sparse_prefill", "sparse_prefill_bits", "plan_upload",
-           "tile_masses", "select_bits", "encode_masses_bytes", "library", "default_scale", "workspace",
-           "device_status", "SIFT_BF16", "SIFT_FP32", "SIFT_DEVICE_OK", "SIFT_DEVICE_PLAN_MISMATCH",
+__all__ = ["Layout", "SiftError", "decode_bits", "decode_bits_noalloc", "sparse_prefill", "sparse_prefill_bits",
+           "plan_upload", "tile_masses", "select_bits", "encode_masses_bytes", "encode_workspace_bytes", "library",
+           "default_scale", "workspace", "device_status", "SIFT_BF16", "SIFT_FP32", "SIFT_DEVICE_OK", "SIFT_DEVICE_PLAN_MISMATCH",
            "SIFT_DEVICE_TILE_RANGE", "SIFT_DEVICE_ROW_RANGE"]

@@ -28,7 +28,7 @@ EXPORTED = (
     "sift_csr_max_nnz", "sift_plan_bytes", "sift_workspace_bytes", "sift_plan_upload",
     "sift_decode_bits", "sift_sparse_prefill", "sift_sparse_prefill_bits", "sift_status_string",
     "sift_abi_version", "sift_encode_masses_bytes", "sift_tile_masses", "sift_select_bits",
-    "sift_device_status", "sift_decode_bits_noalloc",
+    "sift_device_status", "sift_decode_bits_noalloc", "sift_encode_workspace_bytes",
 )
 
 
@@ -83,7 +83,9 @@ def _lib():
     lib.sift_sparse_prefill_bits.restype = ctypes.c_int
     lib.sift_encode_masses_bytes.argtypes = [L]
     lib.sift_encode_masses_bytes.restype = sz
-    lib.sift_tile_masses.argtypes = [L, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
+    lib.sift_encode_workspace_bytes.argtypes = [L]
+    lib.sift_encode_workspace_bytes.restype = sz
+    lib.sift_tile_masses.argtypes = [L, vp, vp, vp, ctypes.c_float, vp, sz, vp, sz, vp, vp]
     lib.sift_tile_masses.restype = ctypes.c_int
     lib.sift_select_bits.argtypes = [L, vp, vp, sz, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp]
     lib.sift_select_bits.restype = ctypes.c_int
@@ -353,12 +355,19 @@ def encode_masses_bytes(layout: Layout) -> int:
     return int(_lib().sift_encode_masses_bytes(layout.ref))
 
 
-def tile_masses(layout: Layout, q, k, plan=None, scale: Optional[float] = None, masses=None, status=None):
+def encode_workspace_bytes(layout: Layout) -> int:
+    return int(_lib().sift_encode_workspace_bytes(layout.ref))
+
+
+def tile_masses(layout: Layout, q, k, plan=None, scale: Optional[float] = None, masses=None, status=None,
+                workspace=None):
     """Per-tile softmax mass of the dense causal attention (offline encoder, first step).
 
     q [N,Hq,D], k [N,Hkv,D] bfloat16.  Returns fp32 masses [Hq, G, RT] (RT = the largest
     request's tile count); entry (h, g, c - first tile of g's request) for the causal c <= g.
     status: optional int32 device tensor of one element for the call's sift_device_flag bits.
+    workspace: optional uint8 device tensor of at least encode_workspace_bytes(layout) bytes
+    (allocated per call when omitted).
     """
     import torch
     device = q.device
@@ -372,12 +381,17 @@ def tile_masses(layout: Layout, q, k, plan=None, scale: Optional[float] = None, 
     _need_tensor("masses", masses, torch.float32, device, min_numel=nbytes // 4)
     if status is not None:
         _need_tensor("status", status, torch.int32, device, min_numel=1)
+    wbytes = encode_workspace_bytes(layout)
+    if workspace is None:
+        workspace = torch.empty(max(wbytes, 256), dtype=torch.uint8, device=device)
+    _need_tensor("workspace", workspace, torch.uint8, device, min_numel=wbytes)
     if plan is None:
         plan = plan_upload(layout, device)
     sc = 0.0 if scale is None else float(scale)
     _check(_lib().sift_tile_masses(
         layout.ref, ctypes.c_void_p(plan.data_ptr()), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
         ctypes.c_float(sc), ctypes.c_void_p(masses.data_ptr()), masses.numel() * masses.element_size(),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
         ctypes.c_void_p(status.data_ptr() if status is not None else 0), _stream_handle(torch, device)),
         "sift_tile_masses")
     return masses

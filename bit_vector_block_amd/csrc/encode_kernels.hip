@@ -52,11 +52,44 @@ __device__ inline f32x16 scores(const bf16x8 (&qf)[D / 16], const char *Kt, int 
     return s;
 }
 
-__device__ inline float wave_sum(float x) {  // fixed butterfly order: deterministic
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
+// The two lanes l and l ^ 32 hold the same query's two key subsets: their sum, and their max, in
+// both lanes (one VALU swap of the wavefront's halves; the same order of addition in both lanes)
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// sum of exp2(score * sl - R) over this lane's 16 keys of key half kh (MASK: keys >= lim count 0)
+template <bool MASK>
+__device__ __forceinline__ float exp_sum(const f32x16 &s, int kh, float sl, float R, int lim, int hi) {
+    const float nr = -R;
+    const int lk = lim - 32 * kh - 4 * hi;  // register i holds a key < lim iff 8 (i / 4) + i % 4 < lk
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float e = __builtin_amdgcn_exp2f(fmaf(s[i], sl, nr));
+        if (MASK) e = 8 * (i >> 2) + (i & 3) < lk ? e : 0.0f;
+        if (i & 1) a1 += e;
+        else a0 += e;
+    }
+    return a0 + a1;
+}
+
+// largest score * sl over this lane's keys < lim of key half kh (-inf if none); sl > 0
+__device__ __forceinline__ float scaled_max(const f32x16 &s, int kh, float sl, int lim, int hi) {
+    const int lk = lim - 32 * kh - 4 * hi;
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + (i & 3) < lk) m = fmaxf(m, s[i]);
+    return m * sl;
+}
+
+constexpr float kRebase = 0x1p64f;  // a tile sum this large moves the reference (entries stay < 2^64)
 
 // K tile c of KV head kvh -> this thread's 64 * D / 8 / NT sixteen-byte chunks, and back out to an
 // LDS tile with rows of 2 D + 16 bytes
@@ -80,140 +113,165 @@ __device__ __forceinline__ void store_k_tile(const uint4 (&stage)[64 * (D / 8) /
     }
 }
 
-// One workgroup per (KV head, group of HPW q heads of it, query tile g): 2 HPW wavefronts, wave w
-// takes q head (group base + w / 2) and queries 32 (w % 2) .. + 31, against all 64 keys of every
-// key tile.  The K tile is loaded once for the HPW heads that share it (GQA) and staged one tile
-// ahead in registers.  Pass 1: each query's running max and sum of exp2; pass 2: each tile's mass.
+// One work item = (KV head, group of HPW q heads of it, query tile g), taken by a persistent
+// workgroup of 2 HPW wavefronts from its XCD's queue, latest query tiles (the longest rows) first.
+// Wave w takes q head (group base + w / 2) and queries 32 (w % 2) .. + 31, against all 64 keys of
+// every key tile; the K tile is loaded once for the HPW heads that share it (GQA) and staged one
+// tile ahead in registers.  One pass over the row's causal key tiles: each query's sum of exp2
+// over a tile's keys, relative to a reference R of that query, goes to the workgroup's scratch
+// slot and into the query's running sum l.  R is the largest scaled score seen when it was last
+// set; it is set again only when a tile's sum reaches 2^64 (or R is still unset), and then the
+// query's earlier entries and l are scaled down to the new R, so every entry shares the final R.
+// The masses are then sum over queries of entry * (1 / l), two wavefronts per head.
 template <int D, int HPW>
 __device__ __forceinline__ void tile_mass_body(const PlanView &pv, const uint16_t *__restrict__ q,
                                                const uint16_t *__restrict__ k, int Hq, int Hkv, float scale_log2,
-                                               float *__restrict__ masses, int RT, int32_t *__restrict__ status) {
-    constexpr int NT = 128 * HPW;
+                                               float *__restrict__ masses, int RT, int *__restrict__ queue,
+                                               float *__restrict__ scratch, int32_t *__restrict__ status) {
+    constexpr int NT = 128 * HPW, W = 2 * HPW;
     constexpr int KROW = 2 * D + 16;
     constexpr int CH = D / 8;              // 16-byte chunks per key row
     constexpr int PER = 64 * CH / NT;      // chunks each thread stages per tile
     static_assert(PER * NT == 64 * CH, "tile chunks split evenly");
+    constexpr int ESTRIDE = W * 32;        // floats per key tile in a scratch slot
     __shared__ __attribute__((aligned(16))) char Kt[2][64 * KROW];
-    __shared__ float part[2][2 * HPW];
+    __shared__ float part[W][64];
+    __shared__ int s_item;
     const bool ok = plan_ok(pv);
     if (status != nullptr && blockIdx.x == 0 && threadIdx.x == 0)  // the call's one writer
         *status = ok ? SIFT_DEVICE_OK : SIFT_DEVICE_PLAN_MISMATCH;
     if (!ok) return;
     const int G = pv.num_tiles;
-    const int group = Hq / Hkv, ngroups = group / HPW;
-    // latest query tiles (the longest rows) first
-    const int g = G - 1 - static_cast<int>(blockIdx.x / (Hkv * ngroups));
-    const int rest = static_cast<int>(blockIdx.x % (Hkv * ngroups));
-    const int kvh = rest / ngroups;
+    const int group = Hq / Hkv, ngroups = group / HPW, per_g = Hkv * ngroups;
+    const int items = G * per_g;
+    const int nq = min(kMassQueues, static_cast<int>(gridDim.x)), xq = static_cast<int>(blockIdx.x) % nq;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-    const int h = kvh * group + (rest % ngroups) * HPW + (wave >> 1);
     const int qi = 32 * (wave & 1) + l32;
-    const int first = pv.req_first[req_of_tile(pv, g)];
-    const int q_valid = pv.tile_valid[g];
-    bf16x8 qf[D / 16];
-    {
-        const uint16_t *qrow = q + ((static_cast<int64_t>(g) * kTile + qi) * Hq + h) * D + 8 * hi;
+    float *const slot = scratch + static_cast<int64_t>(blockIdx.x) * RT * ESTRIDE;
+    float *const mine = slot + wave * 32 + l32;  // this query's entry of key tile e: mine[e * ESTRIDE]
+    for (;;) {
+        if (tid == 0) s_item = xq + nq * atomicAdd(&queue[xq], 1);
+        __syncthreads();
+        const int item = s_item;
+        if (item >= items) break;
+        const int g = G - 1 - item / per_g;
+        const int rest = item % per_g;
+        const int kvh = rest / ngroups;
+        const int h0 = kvh * group + (rest % ngroups) * HPW;  // the item's first q head
+        const int h = h0 + (wave >> 1);
+        const int first = pv.req_first[req_of_tile(pv, g)];
+        const int q_valid = pv.tile_valid[g];
+        const int nt = g - first + 1;
+        bf16x8 qf[D / 16];
+        {
+            const uint16_t *qrow = q + ((static_cast<int64_t>(g) * kTile + qi) * Hq + h) * D + 8 * hi;
 #pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc) qf[dc] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * dc);
-    }
-    // two register stages: the tile after next is loaded while this one is computed and the next
-    // one is waiting to go to LDS
-    uint4 stA[PER], stB[PER];
-    const int nt = g - first + 1;
-    // scaled, masked scores of key half kh of tile c (keys < lim survive)
-    auto tile_scores = [&](int buf, int c, int kh) {
-        f32x16 sc = scores<D>(qf, Kt[buf], kh, l32, hi);
-        const int lim = min(pv.tile_valid[c], c == g ? qi + 1 : kTile);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = 32 * kh + 8 * (i >> 2) + 4 * hi + (i & 3);
-            sc[i] = key < lim ? sc[i] * scale_log2 : -INFINITY;
+            for (int dc = 0; dc < D / 16; ++dc) qf[dc] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * dc);
         }
-        return sc;
-    };
-    // one pass over tiles first .. g: compute(e, buf) sees tile first + e in Kt[buf]
-    auto pass = [&](auto &&compute) {
+        // two register stages: the tile after next is loaded while this one is computed and the
+        // next one is waiting to go to LDS
+        uint4 stA[PER], stB[PER];
+        float R = -INFINITY, l = 0.0f;
         stage_k_tile<D, NT>(stA, k, first, Hkv, kvh, tid);
         store_k_tile<D, NT>(stA, Kt[0], tid);
         if (nt > 1) stage_k_tile<D, NT>(stB, k, first + 1, Hkv, kvh, tid);
         __syncthreads();
+        // key tile first + e is in Kt[buf]; the scores of one key half at a time are live.  Every
+        // score computation runs with the whole wavefront active (an MFMA takes its operands from
+        // all 64 lanes, and each lane reads its own share of the K tile from LDS): the branches
+        // around them are uniform, and lanes that need no new R ignore what they compute.
+        auto step = [&](int e, int buf) {
+            const int c = first + e;
+            const int tv = pv.tile_valid[c];
+            const int lim = c == g ? min(tv, qi + 1) : tv;  // keys < lim count
+            float a = kRebase;                              // R is unset in every lane at e = 0
+            if (e > 0) {
+                if (c != g && tv >= kTile)
+                    a = pair_sum(exp_sum<false>(scores<D>(qf, Kt[buf], 0, l32, hi), 0, scale_log2, R, lim, hi) +
+                                 exp_sum<false>(scores<D>(qf, Kt[buf], 1, l32, hi), 1, scale_log2, R, lim, hi));
+                else
+                    a = pair_sum(exp_sum<true>(scores<D>(qf, Kt[buf], 0, l32, hi), 0, scale_log2, R, lim, hi) +
+                                 exp_sum<true>(scores<D>(qf, Kt[buf], 1, l32, hi), 1, scale_log2, R, lim, hi));
+            }
+            // R unset, or this tile's scores exceed it by ~64 (the two lanes of a query agree)
+            const bool rebase = !(a < kRebase);
+            if (__ballot(rebase) != 0ull) {
+                float mt = scaled_max(scores<D>(qf, Kt[buf], 0, l32, hi), 0, scale_log2, lim, hi);
+                asm volatile("" ::: "memory");  // the halves are computed anew, not kept
+                mt = pair_max(fmaxf(mt, scaled_max(scores<D>(qf, Kt[buf], 1, l32, hi), 1, scale_log2, lim, hi)));
+                const float Rn = fmaxf(R, mt);
+                if (rebase && Rn > R) {
+                    if (R > -INFINITY) {
+                        const float f = __builtin_amdgcn_exp2f(R - Rn);
+                        l *= f;
+                        if (hi == 0)
+                            for (int j = 0; j < e; ++j) mine[j * ESTRIDE] *= f;
+                    }
+                    R = Rn;
+                }
+                asm volatile("" ::: "memory");
+                float a2 = exp_sum<true>(scores<D>(qf, Kt[buf], 0, l32, hi), 0, scale_log2, R, lim, hi);
+                asm volatile("" ::: "memory");
+                a2 = pair_sum(a2 + exp_sum<true>(scores<D>(qf, Kt[buf], 1, l32, hi), 1, scale_log2, R, lim, hi));
+                if (rebase) a = R > -INFINITY ? a2 : 0.0f;
+            }
+            l += a;
+            if (hi == 0) mine[e * ESTRIDE] = a;
+        };
         for (int e = 0; e < nt; e += 2) {
             if (e + 2 < nt) stage_k_tile<D, NT>(stA, k, first + e + 2, Hkv, kvh, tid);
-            compute(e, 0);
+            step(e, 0);
             if (e + 1 < nt) store_k_tile<D, NT>(stB, Kt[1], tid);
             __syncthreads();
             if (e + 1 >= nt) break;
             if (e + 3 < nt) stage_k_tile<D, NT>(stB, k, first + e + 3, Hkv, kvh, tid);
-            compute(e + 1, 1);
+            step(e + 1, 1);
             if (e + 2 < nt) store_k_tile<D, NT>(stA, Kt[0], tid);
             __syncthreads();
         }
-    };
-    // pass 1: running max and sum of exp2 of this lane's query over its keys
-    float m = -INFINITY, l = 0.0f;
-    pass([&](int e, int buf) {
+        // masses: lane (l32, hi) takes key tile e + hi of each pair; padded queries carry no mass
+        const float inv = (qi < q_valid && l > 0.0f) ? 1.0f / l : 0.0f;
+        for (int cb = 0; cb < nt; cb += 64) {
+            const int n = min(64, nt - cb);
+            for (int t = 0; t < n; t += 2) {
+                const bool have = t + hi < n;
+                float v = have ? mine[(cb + t + hi) * ESTRIDE] * inv : 0.0f;
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const f32x16 sc = tile_scores(buf, first + e, kh);
-            float mt = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sc[i]);
-            const float mn = fmaxf(m, mt);
-            if (mn > -INFINITY) {
-                float add = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) add += __builtin_amdgcn_exp2f(sc[i] - mn);
-                l = l * __builtin_amdgcn_exp2f(m - mn) + add;
-                m = mn;
+                for (int off = 16; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);  // within the half
+                if (l32 == 0 && have) part[wave][t + hi] = v;
             }
+            __syncthreads();
+            for (int x = tid; x < HPW * 64; x += NT) {
+                const int hh = x >> 6, t = x & 63;
+                if (t < n)
+                    masses[(static_cast<int64_t>(h0 + hh) * G + g) * RT + cb + t] = part[2 * hh][t] + part[2 * hh + 1][t];
+            }
+            __syncthreads();
         }
-    });
-    {   // lanes l and l ^ 32 hold the same query's two key subsets
-        const float m2 = __shfl_xor(m, 32, 64), l2 = __shfl_xor(l, 32, 64);
-        const float mn = fmaxf(m, m2);
-        l = (mn == -INFINITY) ? 0.0f : l * __builtin_amdgcn_exp2f(m - mn) + l2 * __builtin_amdgcn_exp2f(m2 - mn);
-        m = mn;
     }
-    const float inv = (qi < q_valid && l > 0.0f) ? 1.0f / l : 0.0f;  // padded queries carry no mass
-    // pass 2: every key tile's mass; the two waves of a head are summed (in order) by one thread
-    // at the next step, after the barrier
-    float *row = masses + (static_cast<int64_t>(h - (wave >> 1)) * G + g) * RT;  // the group's first head
-    auto write_tile = [&](int e) {
-        if (tid < HPW) {
-            const float *pp = part[e & 1];
-            row[static_cast<int64_t>(tid) * G * RT + e] = pp[2 * tid] + pp[2 * tid + 1];
-        }
-    };
-    pass([&](int e, int buf) {
-        if (e > 0) write_tile(e - 1);
-        float acc = 0.0f;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const f32x16 sc = tile_scores(buf, first + e, kh);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc += (sc[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[i] - m);
-        }
-        acc = wave_sum(acc * inv);
-        if (lane == 0) part[e & 1][wave] = acc;
-    });
-    write_tile(nt - 1);  // after the last step's barrier
 }
 
 // GQA groups of 2 or 4 q heads per KV head: 4 or 8 wavefronts; four waves per SIMD (the kernel is
 // bound by latency: the resident waves hide each other's loads and barriers)
 template <int D, int HPW>
-__global__ __launch_bounds__(128 * HPW) __attribute__((amdgpu_waves_per_eu(2, 4))) void tile_mass_kernel(
+__global__ __launch_bounds__(128 * HPW) __attribute__((amdgpu_waves_per_eu(4, 4))) void tile_mass_kernel(
     PlanView pv, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, int Hq, int Hkv, float scale_log2,
-    float *__restrict__ masses, int RT, int32_t *__restrict__ status) {
-    tile_mass_body<D, HPW>(pv, q, k, Hq, Hkv, scale_log2, masses, RT, status);
+    float *__restrict__ masses, int RT, int *__restrict__ queue, float *__restrict__ scratch,
+    int32_t *__restrict__ status) {
+    tile_mass_body<D, HPW>(pv, q, k, Hq, Hkv, scale_log2, masses, RT, queue, scratch, status);
 }
 
 // one q head per workgroup (odd groups): two wavefronts stage a whole tile each, so more registers
 template <int D>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 2))) void tile_mass_kernel_one(
     PlanView pv, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, int Hq, int Hkv, float scale_log2,
-    float *__restrict__ masses, int RT, int32_t *__restrict__ status) {
-    tile_mass_body<D, 1>(pv, q, k, Hq, Hkv, scale_log2, masses, RT, status);
+    float *__restrict__ masses, int RT, int *__restrict__ queue, float *__restrict__ scratch,
+    int32_t *__restrict__ status) {
+    tile_mass_body<D, 1>(pv, q, k, Hq, Hkv, scale_log2, masses, RT, queue, scratch, status);
+}
+
+__global__ void mass_queue_reset_kernel(int *__restrict__ queue) {
+    if (threadIdx.x < kMassQueues) queue[threadIdx.x] = 0;
 }
 
 // One wavefront: sort 64 (mass, index) pairs by decreasing mass, ties by increasing index.
@@ -326,25 +384,48 @@ __global__ __launch_bounds__(64 * kSelectWaves) void select_bits_kernel(PlanView
 
 }  // namespace
 
-hipError_t launch_tile_masses(const HostLayout &hl, const PlanView &pv, const uint16_t *q, const uint16_t *k,
-                              float scale, float *masses, int RT, int32_t *status, hipStream_t stream) {
-    if (hl.G == 0) return hipSuccess;
+int mass_heads_per_wg(const HostLayout &hl) {
     const int group = hl.Hq / hl.Hkv;
-    const int hpw = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
-    const unsigned grid = static_cast<unsigned>(int64_t(hl.Hkv) * (group / hpw) * hl.G);
+    return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+}
+
+int64_t mass_slots(const HostLayout &hl) {
+    const int hpw = mass_heads_per_wg(hl);
+    const int64_t items = int64_t(hl.Hkv) * (hl.Hq / hl.Hkv / hpw) * hl.G;
+    return std::min<int64_t>(items, kMassWaves / (2 * hpw));
+}
+
+size_t mass_workspace_bytes(const HostLayout &hl) {
+    const int64_t rt = hl.max_req_tiles > 0 ? hl.max_req_tiles : 1;
+    return kWorkspaceHeader + size_t(mass_slots(hl)) * size_t(rt) * size_t(mass_heads_per_wg(hl)) * 64 * sizeof(float);
+}
+
+hipError_t launch_tile_masses(const HostLayout &hl, const PlanView &pv, const uint16_t *q, const uint16_t *k,
+                              float scale, float *masses, int RT, void *workspace, int32_t *status,
+                              hipStream_t stream) {
+    if (hl.G == 0) return hipSuccess;
+    const int hpw = mass_heads_per_wg(hl);
+    const unsigned grid = static_cast<unsigned>(mass_slots(hl));
+    int *queue = static_cast<int *>(workspace);
+    float *scratch = reinterpret_cast<float *>(static_cast<char *>(workspace) + kWorkspaceHeader);
     const float sl = scale * 1.4426950408889634f;
-#define SIFT_TILE_MASS(DD, HH) \
-    tile_mass_kernel<DD, HH><<<grid, 128 * HH, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT, status)
+    mass_queue_reset_kernel<<<1, 64, 0, stream>>>(queue);
+#define SIFT_TILE_MASS(DD, HH)                                                                                   \
+    tile_mass_kernel<DD, HH><<<grid, 128 * HH, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT, queue, scratch, \
+                                                            status)
+#define SIFT_TILE_MASS_ONE(DD) \
+    tile_mass_kernel_one<DD><<<grid, 128, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT, queue, scratch, status)
     if (hl.D == 128) {
         if (hpw == 4) SIFT_TILE_MASS(128, 4);
         else if (hpw == 2) SIFT_TILE_MASS(128, 2);
-        else tile_mass_kernel_one<128><<<grid, 128, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT, status);
+        else SIFT_TILE_MASS_ONE(128);
     } else {
         if (hpw == 4) SIFT_TILE_MASS(64, 4);
         else if (hpw == 2) SIFT_TILE_MASS(64, 2);
-        else tile_mass_kernel_one<64><<<grid, 128, 0, stream>>>(pv, q, k, hl.Hq, hl.Hkv, sl, masses, RT, status);
+        else SIFT_TILE_MASS_ONE(64);
     }
 #undef SIFT_TILE_MASS
+#undef SIFT_TILE_MASS_ONE
     return hipGetLastError();
 }
 

@@ -245,7 +245,7 @@ using namespace sift;
 
 extern "C" {
 
-int32_t sift_abi_version(void) { return (2 << 16) | 0; }
+int32_t sift_abi_version(void) { return (3 << 16) | 0; }
 
 const char *sift_status_string(sift_status s) {
     switch (s) {
@@ -462,22 +462,29 @@ size_t sift_encode_masses_bytes(const sift_layout *layout) {
     return sizeof(float) * size_t(hl.Hq) * size_t(hl.G) * size_t(hl.max_req_tiles > 0 ? hl.max_req_tiles : 1);
 }
 
+size_t sift_encode_workspace_bytes(const sift_layout *layout) {
+    HostLayout hl;
+    if (build_layout(layout, &hl) != SIFT_OK) return 0;
+    return mass_workspace_bytes(hl);
+}
+
 sift_status sift_tile_masses(const sift_layout *layout, const void *d_plan, const void *d_q, const void *d_k,
-                             float scale, float *d_masses, size_t masses_bytes, int32_t *d_status,
-                             hipStream_t stream) {
+                             float scale, float *d_masses, size_t masses_bytes, void *d_workspace,
+                             size_t workspace_bytes, int32_t *d_status, hipStream_t stream) {
     HostLayout hl;
     sift_status st = build_layout(layout, &hl);
     if (st != SIFT_OK) return st;
     if (hl.G == 0) return SIFT_OK;
     if (!d_plan || !d_q || !d_k || !d_masses) return SIFT_ERR_INVALID;
     auto aligned16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-    if (!aligned16(d_q) || !aligned16(d_k)) return SIFT_ERR_INVALID;
+    if (!aligned16(d_q) || !aligned16(d_k) || (d_workspace && !aligned16(d_workspace))) return SIFT_ERR_INVALID;
     if (!(scale > 0.0f)) scale = 1.0f / sqrtf(float(hl.D));
     if (!isfinite(scale)) return SIFT_ERR_INVALID;
     if (masses_bytes < sift_encode_masses_bytes(layout)) return SIFT_ERR_CAPACITY;
+    if (!d_workspace || workspace_bytes < mass_workspace_bytes(hl)) return SIFT_ERR_CAPACITY;
     const PlanView pv = plan_view(hl, d_plan);
     if (launch_tile_masses(hl, pv, static_cast<const uint16_t *>(d_q), static_cast<const uint16_t *>(d_k), scale,
-                           d_masses, static_cast<int>(hl.max_req_tiles), d_status, stream) != hipSuccess)
+                           d_masses, static_cast<int>(hl.max_req_tiles), d_workspace, d_status, stream) != hipSuccess)
         return SIFT_ERR_HIP;
     return SIFT_OK;
 }

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "sift.h"
@@ -77,8 +78,16 @@ hipError_t launch_bits_prepass(const HostLayout &hl, const PlanView &pv, const u
                                int32_t *ca_prefix, int32_t *ca_list, int32_t *rowinfo, hipStream_t stream);
 // Offline encoder (tile masses of dense attention, then top-p selection into LA/CA words).
 // `status` (may be null): the caller's device word for the sift_device_flag bits.
+// The tile-mass kernel is persistent: each workgroup claims work items from its XCD's queue
+// (the first kMassQueues ints of the workspace, cleared by the launch) and keeps its queries'
+// per-tile sums in its own slot of the workspace (past the 256-byte header).
+constexpr int kMassQueues = 8;    // one work queue per XCD
+constexpr int kMassWaves = 4096;  // wavefronts the persistent grid is sized for: 256 CUs x 16
+int64_t mass_slots(const HostLayout &hl);
+size_t mass_workspace_bytes(const HostLayout &hl);
 hipError_t launch_tile_masses(const HostLayout &hl, const PlanView &pv, const uint16_t *q, const uint16_t *k,
-                              float scale, float *masses, int RT, int32_t *status, hipStream_t stream);
+                              float scale, float *masses, int RT, void *workspace, int32_t *status,
+                              hipStream_t stream);
 hipError_t launch_select_bits(const HostLayout &hl, const PlanView &pv, const float *masses, int RT, float p_la,
                               float p_ca, uint32_t *la_out, uint32_t *ca_out, int32_t *status, hipStream_t stream);
 hipError_t launch_cast_bf16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);

@@ -238,7 +238,11 @@ sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_pl
  * Q [N][Hq][D] and K [N][Hkv][D], 16-byte aligned; scale <= 0 selects 1/sqrt(head_dim)).
  * d_masses: fp32 [Hq][G][RT], RT = the largest request's tile count; entry (h, g, c - first)
  * with first = the first tile of g's request, written for first <= c <= g only.  masses_bytes >=
- * sift_encode_masses_bytes(layout).
+ * sift_encode_masses_bytes(layout).  The scores are computed once: each query's per-tile sums of
+ * exp2 go to d_workspace (>= sift_encode_workspace_bytes(layout) bytes, 16-byte aligned; about
+ * 512 KiB per tile of the largest request: a slot per resident workgroup, not per work item),
+ * and are weighted by the query's 1 / (row sum) once its row is done.  Calls that run at the
+ * same time need separate workspaces.
  *
  * sift_select_bits: LA row r of document d keeps its candidate tiles c <= r by decreasing mass
  * (ties: smaller c) up to the first prefix whose mass reaches p_la of their total, plus tiles r
@@ -246,17 +250,19 @@ sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_pl
  * (summed in increasing tile order) and the pages are kept the same way with p_ca, plus page 0.
  * The threshold test sums in float32 in a fixed order (an inclusive Hillis-Steele scan of the
  * sorted masses).  Writes every word of d_la / d_ca (layout as for sift_decode_bits).
- * Errors: SIFT_ERR_INVALID (p outside (0, 1], nulls), SIFT_ERR_CAPACITY (masses_bytes),
- * SIFT_ERR_UNSUPPORTED (a document of more than 64 tiles), SIFT_ERR_HIP.
+ * Errors: SIFT_ERR_INVALID (p outside (0, 1], nulls, misaligned pointers), SIFT_ERR_CAPACITY
+ * (masses_bytes, workspace), SIFT_ERR_UNSUPPORTED (sift_select_bits: a document of more than 64
+ * tiles), SIFT_ERR_HIP.
  *
  * d_status (both calls, may be NULL): one device int32 that the call sets to SIFT_DEVICE_OK, or to
  * SIFT_DEVICE_PLAN_MISMATCH when d_plan holds another layout's plan (the outputs are then left
  * untouched).  A call with nothing to do (no tiles, no documents) leaves it as it is.
  */
 size_t sift_encode_masses_bytes(const sift_layout *layout);
+size_t sift_encode_workspace_bytes(const sift_layout *layout);
 sift_status sift_tile_masses(const sift_layout *layout, const void *d_plan, const void *d_q, const void *d_k,
-                             float scale, float *d_masses, size_t masses_bytes, int32_t *d_status,
-                             hipStream_t stream);
+                             float scale, float *d_masses, size_t masses_bytes, void *d_workspace,
+                             size_t workspace_bytes, int32_t *d_status, hipStream_t stream);
 sift_status sift_select_bits(const sift_layout *layout, const void *d_plan, const float *d_masses,
                              size_t masses_bytes, float p_la, float p_ca, uint32_t *d_la, uint32_t *d_ca,
                              int32_t *d_status, hipStream_t stream);

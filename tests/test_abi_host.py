@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTED) == declared
-    assert lib.sift_abi_version() >> 16 == 2
+    assert lib.sift_abi_version() >> 16 == 3
 
 
 @pytest.mark.parametrize("cid", [1, 2])
@@ -188,7 +188,7 @@ def test_encoder_validation():
     case = W.random_small_case(4, d=64)
     lay = sift.Layout.from_case(case)
     lib = sift.library()
-    vp, f = ctypes.c_void_p, ctypes.c_float
+    vp, f, sz = ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
     a = vp(4096)
     need = lib.sift_encode_masses_bytes(lay.ref)
     tiles = [-(-int(n) // 64) for n in case.doc_len]
@@ -197,9 +197,21 @@ def test_encoder_validation():
         rt = max(rt, sum(tiles[d0:d0 + k]) + -(-int(case.question_len[b]) // 64))
         d0 += k
     assert need == 4 * lay.num_q_heads * lay.num_tiles * rt
-    assert lib.sift_tile_masses(lay.ref, a, vp(0), a, f(0.0), a, need, vp(0), vp(0)) == B.SIFT_ERR_INVALID
-    assert lib.sift_tile_masses(lay.ref, a, vp(4104), a, f(0.0), a, need, vp(0), vp(0)) == B.SIFT_ERR_INVALID
-    assert lib.sift_tile_masses(lay.ref, a, a, a, f(0.0), a, need - 4, vp(0), vp(0)) == B.SIFT_ERR_CAPACITY
+    # the workspace: a 256-byte header, then one slot per persistent workgroup (2 hpw wavefronts,
+    # 4096 wavefronts in all, never more than the work items) of rt tiles x hpw heads x 64 queries
+    group = lay.num_q_heads // lay.num_kv_heads
+    hpw = 4 if group % 4 == 0 else (2 if group % 2 == 0 else 1)
+    slots = min(lay.num_kv_heads * (group // hpw) * lay.num_tiles, 4096 // (2 * hpw))
+    wneed = lib.sift_encode_workspace_bytes(lay.ref)
+    assert wneed == 256 + slots * rt * hpw * 64 * 4
+    z = sz(wneed)
+    tm = lib.sift_tile_masses
+    assert tm(lay.ref, a, vp(0), a, f(0.0), a, need, a, z, vp(0), vp(0)) == B.SIFT_ERR_INVALID
+    assert tm(lay.ref, a, vp(4104), a, f(0.0), a, need, a, z, vp(0), vp(0)) == B.SIFT_ERR_INVALID
+    assert tm(lay.ref, a, a, a, f(0.0), a, need, vp(4100), z, vp(0), vp(0)) == B.SIFT_ERR_INVALID
+    assert tm(lay.ref, a, a, a, f(0.0), a, need - 4, a, z, vp(0), vp(0)) == B.SIFT_ERR_CAPACITY
+    assert tm(lay.ref, a, a, a, f(0.0), a, need, a, sz(wneed - 4), vp(0), vp(0)) == B.SIFT_ERR_CAPACITY
+    assert tm(lay.ref, a, a, a, f(0.0), a, need, vp(0), z, vp(0), vp(0)) == B.SIFT_ERR_CAPACITY
     for p_la, p_ca in ((0.0, 0.5), (0.5, 1.5), (float("nan"), 0.5)):
         assert lib.sift_select_bits(lay.ref, a, a, need, f(p_la), f(p_ca), a, a, vp(0), vp(0)) == B.SIFT_ERR_INVALID
     assert lib.sift_select_bits(lay.ref, a, a, need - 4, f(0.9), f(0.9), a, a, vp(0), vp(0)) == B.SIFT_ERR_CAPACITY
@@ -267,6 +279,8 @@ def test_binding_rejects_bad_output_and_csr_tensors():
         sift.tile_masses(lay, q, k, masses=torch.empty(3, dtype=torch.float32))
     with pytest.raises(ValueError):
         sift.tile_masses(lay, q, k, status=torch.empty(1, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        sift.tile_masses(lay, q, k, workspace=torch.empty(8, dtype=torch.uint8))
 
 
 def test_noalloc_decode_rejects_a_layout_beyond_its_scratch():

@@ -142,6 +142,27 @@ def test_masses_gqa_groupings(seed, hq, hkv, d):
     _assert_masses(case, _full(case, m.cpu().numpy()), E.tile_masses(case))
 
 
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (2, 1), (1, 1)])
+def test_masses_with_score_jumps(hq, hkv):
+    """Key tiles scaled by powers of two (exact in bf16): a query's largest score jumps by far
+    more than 64 (in log2 units) from one tile to the next and falls back after, so the kernel
+    moves its reference several times within a row, scales the entries it already holds (some of
+    them to zero), and the masses still match the oracle's.  Pairs of neighbouring tiles share a
+    scale, so the mass of a row splits between tiles stored before and after a move.  One request
+    of 11 tiles, two documents and a question."""
+    rng = np.random.default_rng(31)
+    case = W.make_case("jumps", 31, [2], [64 * 5, 64 * 4 - 9], [90], hq, hkv, 64,
+                       np.full((1, hq), 0.3), np.full((1, hq), 0.3), rng=rng)
+    k = W.bf16_bits_to_f32(case.k)
+    for t, f in enumerate([1, 64, 1, 256, 256, 1, 1024, 1024, 4, 1, 1]):
+        k[64 * t:64 * (t + 1)] *= f
+    case.k = W.f32_to_bf16_bits(k)
+    assert np.array_equal(W.bf16_bits_to_f32(case.k), k)  # the scaling is exact
+    print(f"encoder score jumps hq={hq} hkv={hkv}", flush=True)
+    lay, plan, m = _gpu_masses(case)
+    _assert_masses(case, _full(case, m.cpu().numpy()), E.tile_masses(case))
+
+
 def _long_doc_case(doc_tiles, seed=5):
     """One request, documents of the given tile counts (the last one ragged), a short question."""
     lens = [64 * t for t in doc_tiles]
