@@ -177,7 +177,7 @@ __device__ __forceinline__ void load_vt_tile(const uint16_t *base, char *dst, in
 
 __device__ inline float pair_max(float x) {  // max over lanes l and l ^ 32
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ inline float pair_sum(float x) {  // sum over lanes l and l ^ 32
@@ -185,9 +185,11 @@ __device__ inline float pair_sum(float x) {  // sum over lanes l and l ^ 32
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// max of three (v_max3_f32).  Plain code, not inline asm: the inputs are MFMA results, and
+// max of three (v_maximum3_f32).  Plain code, not inline asm: the inputs are MFMA results, and
 // only the compiler's hazard tracking inserts the wait states a VALU read of an MFMA result needs.
-__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
 
 // Online-softmax state of one wavefront (32 queries x one 32-key half of each tile).
 template <int D>
