@@ -91,26 +91,54 @@ __device__ __forceinline__ float scaled_max(const f32x16 &s, int kh, float sl, i
 
 constexpr float kRebase = 0x1p64f;  // a tile sum this large moves the reference (entries stay < 2^64)
 
-// K tile c of KV head kvh -> this thread's 64 * D / 8 / NT sixteen-byte chunks, and back out to an
-// LDS tile with rows of 2 D + 16 bytes
-template <int D, int NT>
-__device__ __forceinline__ void stage_k_tile(uint4 (&stage)[64 * (D / 8) / NT], const uint16_t *__restrict__ k, int c,
-                                             int Hkv, int kvh, int tid) {
-    constexpr int CH = D / 8;
+// K tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds): one load writes lane i's
+// 16 bytes at byte 16 i of a 1 KB LDS block, so the row padding of the LDS layout (rows of
+// 2 D + 16 bytes) is applied on the global side: lane i fetches the chunk that belongs at its LDS
+// position.  A K tile is 64 rows of 2 D + 16 bytes, 17 (D = 128) or 9 (D = 64) such blocks; wave
+// w of W issues blocks w, w + W, ...  A lane whose position is a row's padding fetches chunk 0 of
+// that row again (never read).
+template <int D, int W>
+struct KLds {
+    static constexpr int KROW = 2 * D + 16, CPR = D / 8;
+    static constexpr int BLOCKS = 64 * KROW / 1024;
+    static constexpr int PERW = (BLOCKS + W - 1) / W;
+    static_assert(64 * KROW % 1024 == 0, "whole 1 KB blocks");
+};
+
+template <int D, int W>
+__device__ inline void k_lds_offsets(uint32_t *off, int Hkv, int wave, int lane) {  // off: KLds::PERW entries
+    using C = KLds<D, W>;
+    const uint32_t row_bytes = static_cast<uint32_t>(Hkv) * D * 2;
 #pragma unroll
-    for (int j = 0; j < 64 * CH / NT; ++j) {
-        const int x = tid + j * NT, r = x / CH, ch = x % CH;
-        stage[j] = *reinterpret_cast<const uint4 *>(k + ((static_cast<int64_t>(c) * kTile + r) * Hkv + kvh) * D + 8 * ch);
+    for (int j = 0; j < C::PERW; ++j) {
+        const int b = 1024 * (wave + W * j) + 16 * lane;  // the LDS byte this lane fills
+        const int r = b / C::KROW, c = (b % C::KROW) / 16;
+        off[j] = r * row_bytes + 16u * static_cast<uint32_t>(c < C::CPR ? c : 0);
     }
 }
-template <int D, int NT>
-__device__ __forceinline__ void store_k_tile(const uint4 (&stage)[64 * (D / 8) / NT], char *Kt, int tid) {
-    constexpr int CH = D / 8, KROW = 2 * D + 16;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct-to-LDS load of K tile c of KV head kvh into dst (the tile's base address sits in the
+// buffer descriptor, scalar registers; each lane supplies its 32-bit offset).
+template <int D, int W>
+__device__ __forceinline__ void load_k_lds(const uint16_t *__restrict__ k, int c, int Hkv, int kvh, char *dst, int wave,
+                                           const uint32_t *off) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot type-check these builtins
+    using C = KLds<D, W>;
+    const uint16_t *base = k + (static_cast<int64_t>(c) * kTile * Hkv + kvh) * D;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), 0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < 64 * CH / NT; ++j) {
-        const int x = tid + j * NT, r = x / CH, ch = x % CH;
-        *reinterpret_cast<uint4 *>(Kt + r * KROW + 16 * ch) = stage[j];
-    }
+    for (int j = 0; j < C::PERW; ++j)
+        if (wave + W * j < C::BLOCKS)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + 1024 * (wave + W * j)), 16,
+                                                     static_cast<int>(off[j]), 0, 0, 0);
+#endif
+}
+
+__device__ inline void wait_vmcnt0() {  // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
 }
 
 // One work item = (KV head, group of HPW q heads of it, query tile g), taken by a persistent
@@ -130,9 +158,6 @@ __device__ __forceinline__ void tile_mass_body(const PlanView &pv, const uint16_
                                                float *__restrict__ scratch, int32_t *__restrict__ status) {
     constexpr int NT = 128 * HPW, W = 2 * HPW;
     constexpr int KROW = 2 * D + 16;
-    constexpr int CH = D / 8;              // 16-byte chunks per key row
-    constexpr int PER = 64 * CH / NT;      // chunks each thread stages per tile
-    static_assert(PER * NT == 64 * CH, "tile chunks split evenly");
     constexpr int ESTRIDE = W * 32;        // floats per key tile in a scratch slot
     __shared__ __attribute__((aligned(16))) char Kt[2][64 * KROW];
     __shared__ float part[W][64];
@@ -149,6 +174,9 @@ __device__ __forceinline__ void tile_mass_body(const PlanView &pv, const uint16_
     const int qi = 32 * (wave & 1) + l32;
     float *const slot = scratch + static_cast<int64_t>(blockIdx.x) * RT * ESTRIDE;
     float *const mine = slot + wave * 32 + l32;  // this query's entry of key tile e: mine[e * ESTRIDE]
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t koff[KLds<D, W>::PERW];
+    k_lds_offsets<D, W>(koff, Hkv, uwave, lane);
     for (;;) {
         if (tid == 0) s_item = xq + nq * atomicAdd(&queue[xq], 1);
         __syncthreads();
@@ -168,14 +196,11 @@ __device__ __forceinline__ void tile_mass_body(const PlanView &pv, const uint16_
 #pragma unroll
             for (int dc = 0; dc < D / 16; ++dc) qf[dc] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * dc);
         }
-        // two register stages: the tile after next is loaded while this one is computed and the
-        // next one is waiting to go to LDS
-        uint4 stA[PER], stB[PER];
+        // K(first) now; at the start of every step, a wait for this wave's loads and a barrier
+        // (K(e) has landed, every wave has left step e - 1), then K(e + 1) goes into the buffer
+        // that step e - 1 used, one step ahead of its use
+        load_k_lds<D, W>(k, first, Hkv, kvh, Kt[0], uwave, koff);
         float R = -INFINITY, l = 0.0f;
-        stage_k_tile<D, NT>(stA, k, first, Hkv, kvh, tid);
-        store_k_tile<D, NT>(stA, Kt[0], tid);
-        if (nt > 1) stage_k_tile<D, NT>(stB, k, first + 1, Hkv, kvh, tid);
-        __syncthreads();
         // key tile first + e is in Kt[buf]; the scores of one key half at a time are live.  Every
         // score computation runs with the whole wavefront active (an MFMA takes its operands from
         // all 64 lanes, and each lane reads its own share of the K tile from LDS): the branches
@@ -219,15 +244,15 @@ __device__ __forceinline__ void tile_mass_body(const PlanView &pv, const uint16_
             if (hi == 0) mine[e * ESTRIDE] = a;
         };
         for (int e = 0; e < nt; e += 2) {
-            if (e + 2 < nt) stage_k_tile<D, NT>(stA, k, first + e + 2, Hkv, kvh, tid);
+            wait_vmcnt0();
+            __syncthreads();
+            if (e + 1 < nt) load_k_lds<D, W>(k, first + e + 1, Hkv, kvh, Kt[1], uwave, koff);
             step(e, 0);
-            if (e + 1 < nt) store_k_tile<D, NT>(stB, Kt[1], tid);
-            __syncthreads();
             if (e + 1 >= nt) break;
-            if (e + 3 < nt) stage_k_tile<D, NT>(stB, k, first + e + 3, Hkv, kvh, tid);
-            step(e + 1, 1);
-            if (e + 2 < nt) store_k_tile<D, NT>(stA, Kt[0], tid);
+            wait_vmcnt0();
             __syncthreads();
+            if (e + 2 < nt) load_k_lds<D, W>(k, first + e + 2, Hkv, kvh, Kt[0], uwave, koff);
+            step(e + 1, 1);
         }
         // masses: lane (l32, hi) takes key tile e + hi of each pair; padded queries carry no mass
         const float inv = (qi < q_valid && l > 0.0f) ? 1.0f / l : 0.0f;
