@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["sift_api.hip", "decode_kernels.hip", "prefill_kernels.hip", "encode_kernels.hip"]
+SOURCES = ["sift_api.hip", "decode_kernels.hip", "prepare_kernels.hip", "prefill_kernels.hip", "encode_kernels.hip"]
 OUT = os.path.join(HERE, "libsift.so")
 # the MFMA throughput probe bench.py measures the attention kernel against (not the prefill path)
 PROBE_SOURCES = ["mfma_probe.hip"]

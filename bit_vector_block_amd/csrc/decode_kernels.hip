@@ -20,28 +20,17 @@
 //                 one lane per bit: ballot gives the set mask, mbcnt the
 //                 lane's rank among the set bits, so the 64 lanes write their
 //                 tile ids in order with no atomics.
+#include "bits_common.hpp"
 #include "sift_internal.hpp"
 
 namespace sift {
 
 namespace {
 
-constexpr int kCountThreads = 256;
+using namespace bits;
+
 constexpr int kFillWaves = 4;
 
-
-// Number of set bits among bits [lo, hi] (inclusive) of a word array.
-__device__ inline int popcount_range(const uint32_t *vec, int lo, int hi) {
-    int cnt = 0;
-    for (int w = lo >> 5; w <= (hi >> 5); ++w) {
-        const int b0 = max(lo, w << 5) - (w << 5);
-        const int b1 = min(hi, (w << 5) + 31) - (w << 5);
-        const uint32_t upper = (b1 == 31) ? 0xffffffffu : ((1u << (b1 + 1)) - 1u);
-        const uint32_t mask = upper & ~((1u << b0) - 1u);
-        cnt += __popc(vec[w] & mask);
-    }
-    return cnt;
-}
 
 __device__ inline int row_count(const PlanView &pv, const uint32_t *la, const int32_t *ca_prefix_h,
                                 int h, int g) {
@@ -51,79 +40,6 @@ __device__ inline int row_count(const PlanView &pv, const uint32_t *la, const in
     const uint32_t *vec = la + pv.doc_la_off[d] + h * pv.doc_la_w[d];
     const int lo = r * (r + 1) / 2;
     return ca_prefix_h[d] + popcount_range(vec, lo, lo + r);
-}
-
-// Exclusive scan of one int per thread over a workgroup of kCountThreads threads (wave scans, then
-// the wave totals through sh[kCountThreads / 64]); total gets the workgroup's sum.  Every thread
-// of the workgroup calls it.
-__device__ inline int block_excl_scan(int x, int *sh, int &total) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int incl = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-    }
-    if (lane == 63) sh[wave] = incl;
-    __syncthreads();
-    int below = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < kCountThreads / 64; ++w) {
-        const int v = sh[w];
-        below += w < wave ? v : 0;
-        all += v;
-    }
-    __syncthreads();  // sh is free again
-    total = all;
-    return below + incl - x;
-}
-
-// pref[d] = CA entries of the earlier documents of d's request, for q head h: the CA popcounts of
-// all documents scanned in chunks of kCountThreads, then each document's value less that of its
-// request's first document.  tmp: >= ndocs ints of scratch in global memory.
-__device__ inline void head_ca_prefix(const PlanView &pv, const uint32_t *__restrict__ ca, int h, int32_t *pref,
-                                      int32_t *tmp, int *sh) {
-    const int tid = threadIdx.x, ndocs = pv.num_docs;
-    int carry = 0;
-    for (int base = 0; base < ndocs; base += kCountThreads) {
-        const int d = base + tid;
-        const int c = d < ndocs ? popcount_range(ca + pv.doc_ca_off[d] + h * pv.doc_ca_w[d], 0, pv.doc_tiles[d] - 1)
-                                : 0;
-        int total;
-        const int ex = block_excl_scan(c, sh, total);
-        if (d < ndocs) tmp[d] = carry + ex;  // CA entries of every earlier document of the batch
-        carry += total;
-    }
-    __syncthreads();
-    for (int d = tid; d < ndocs; d += kCountThreads) pref[d] = tmp[d] - tmp[pv.req_first_doc[pv.doc_req[d]]];
-    __syncthreads();
-}
-
-__device__ inline int lane_rank(uint64_t mask) {
-    // number of set bits of `mask` below this lane
-    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
-                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
-}
-
-// lst[req_first[b] + k] = the k-th CA-marked page of request b for q head h, in document order (the
-// CA part of every document row of the request is a leading slice of it).  One thread per
-// document walks its set bits in order, so all documents proceed at once.  pref from
-// head_ca_prefix.
-__device__ inline void head_ca_list(const PlanView &pv, const uint32_t *__restrict__ ca, int h,
-                                    const int32_t *pref, int32_t *lst) {
-    for (int d = threadIdx.x; d < pv.num_docs; d += kCountThreads) {
-        const uint32_t *vec = ca + pv.doc_ca_off[d] + h * pv.doc_ca_w[d];
-        const int T = pv.doc_tiles[d], t0 = pv.doc_first[d];
-        int pos = pv.req_first[pv.doc_req[d]] + pref[d];
-        for (int w = 0; 32 * w < T; ++w) {
-            uint32_t bits = vec[w];
-            if (T - 32 * w < 32) bits &= (1u << (T - 32 * w)) - 1u;  // bits past T are ignored
-            while (bits != 0u) {
-                lst[pos++] = t0 + 32 * w + __builtin_ctz(bits);
-                bits &= bits - 1u;
-            }
-        }
-    }
 }
 
 __global__ __launch_bounds__(kCountThreads) void decode_count_kernel(
@@ -228,62 +144,7 @@ __global__ __launch_bounds__(64 * kFillWaves) void decode_fill_kernel(
     }
 }
 
-// Pre-pass of the fused path (no CSR): one workgroup per q head h.
-//   ca_prefix[h][d] : CA entries of the earlier documents of d's request (request-local);
-//   ca_list[h][req_first[b] + k] : the k-th CA-marked page of request b, in document order --
-//                      the CA part of every document row of the request is a leading slice of it;
-//   rowinfo[h][g]   : what the attention kernel needs to build row (h, g)'s list itself:
-//                      {n, ca_n (-1: question row, dense range), ca_base, la_word, la_lo, t0, r, 0}.
-__global__ __launch_bounds__(kCountThreads) void bits_prepass_kernel(
-    PlanView pv, const uint32_t *__restrict__ la, const uint32_t *__restrict__ ca,
-    int32_t *__restrict__ ca_prefix, int32_t *__restrict__ ca_list, int32_t *__restrict__ rowinfo) {
-    if (!plan_ok(pv)) return;
-    const int h = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int ndocs = pv.num_docs, G = pv.num_tiles;
-    int32_t *pref = ca_prefix + static_cast<int64_t>(h) * ndocs;
-    int32_t *lst = ca_list + static_cast<int64_t>(h) * G;
-    __shared__ int sh[kCountThreads / 64];
-    head_ca_prefix(pv, ca, h, pref, lst, sh);  // the head's page list (G >= ndocs) as scratch
-    head_ca_list(pv, ca, h, pref, lst);
-    // per-row records
-    for (int g = tid; g < G; g += kCountThreads) {
-        int32_t *ri = rowinfo + (static_cast<int64_t>(h) * G + g) * 8;
-        const int d = pv.tile_doc[g];
-        if (d < 0) {
-            const int first = pv.req_first[-d - 1];
-            ri[0] = g - first + 1;
-            ri[1] = -1;
-            ri[2] = 0;
-            ri[3] = 0;
-            ri[4] = 0;
-            ri[5] = first;
-            ri[6] = 0;
-        } else {
-            const int r = pv.tile_local[g];
-            const int lo = r * (r + 1) / 2;
-            const int la_word = pv.doc_la_off[d] + h * pv.doc_la_w[d];
-            const int la_n = popcount_range(la + la_word, lo, lo + r);
-            ri[0] = pref[d] + la_n;
-            ri[1] = pref[d];
-            ri[2] = h * G + pv.req_first[pv.doc_req[d]];
-            ri[3] = la_word;
-            ri[4] = lo;
-            ri[5] = pv.doc_first[d];
-            ri[6] = r;
-        }
-        ri[7] = 0;
-    }
-}
-
 }  // namespace
-
-hipError_t launch_bits_prepass(const HostLayout &hl, const PlanView &pv, const uint32_t *la, const uint32_t *ca,
-                               int32_t *ca_prefix, int32_t *ca_list, int32_t *rowinfo, hipStream_t stream) {
-    if (hl.G == 0) return hipSuccess;
-    bits_prepass_kernel<<<hl.Hq, kCountThreads, 0, stream>>>(pv, la, ca, ca_prefix, ca_list, rowinfo);
-    return hipGetLastError();
-}
 
 hipError_t launch_decode(const HostLayout &hl, const PlanView &pv, const uint32_t *la,
                          const uint32_t *ca, int32_t *row_ptr, int32_t *col_idx, void *scratch,

@@ -6,14 +6,15 @@
 // MI355X-native design, not the FlashAttention-3 (Hopper) kernel the pages
 // build on:
 //
-//  * one workgroup = one CSR row (q head h, query tile g) = 64 queries, four
-//    wavefronts: wave w takes queries 32 (w & 1) .. +31 and, of every listed
-//    KV tile, keys 32 (w >> 1) .. +31.  Each wave keeps its own online-softmax
-//    state; the two key halves are merged once at the end;
-//  * V is first rewritten as V^T ([kv head][D][N], one pass over V per call)
-//    with the tokens of every 16-token group stored in the order the PV
-//    operands consume them, so that every MFMA operand -- K for the scores,
-//    V^T for the output -- is one 16-byte LDS read per lane;
+//  * a CSR row (q head h, query tile g) = 64 queries is handled by one workgroup
+//    of four wavefronts: wave w takes queries 32 (w & 1) .. +31 and, of every
+//    listed KV tile, keys 32 (w >> 1) .. +31.  Each wave keeps its own
+//    online-softmax state; the two key halves are merged once at the end;
+//  * V arrives as V^T ([kv head][D][N], bf16), written by transpose_v_kernel
+//    (prepare_kernels.hip) before this kernel, with the tokens of every
+//    16-token group stored in the order the PV operands consume them, so
+//    that every MFMA operand -- K for the scores, V^T for the output -- is one
+//    16-byte LDS read per lane;
 //  * K and V^T tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds:
 //    the tile's base address in a scalar buffer descriptor, a 32-bit offset per
 //    lane, no register staging), double buffered so the next listed tile streams in
@@ -35,8 +36,11 @@
 //    never leaks;
 //  * P is rounded to bf16 for the PV product and l sums the same rounded
 //    values (v_dot2_f32_bf16 against ones);
-//  * rows are assigned to workgroups KV-head-major, one contiguous share per
-//    XCD, longest rows (latest query tiles) first.
+//  * the kernel is persistent (two workgroups per CU): each workgroup claims
+//    rows with an atomic counter from its XCD's queue over the KV-head-major
+//    row order (longest rows, i.e. latest query tiles, first), and helps the
+//    other XCDs' queues once its own is exhausted; the next row's claim,
+//    metadata, Q and first K/V^T tiles are fetched while the current row runs.
 #include <math.h>
 
 #include <algorithm>
@@ -66,6 +70,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLazyLog2 = 8.0f;
 constexpr int kXcds = 8;
+static_assert(kXcds == kPrefillQueues, "one row queue per XCD");
 constexpr int kPersistentPerXcd = 64;  // 2 workgroups on each of the 32 CUs of an XCD
 
 
@@ -86,11 +91,6 @@ struct Cfg {
 // slot of 16-byte chunk c in V^T row d (64 tokens = 8 chunks per row): the 16 lanes of one
 // LDS cycle read rows d0 .. d0 + 15 at one chunk; (d & 1, (d >> 1) & 7) is distinct over them
 __device__ inline int vt_slot(int d, int c) { return c ^ ((d >> 1) & 7); }
-
-// position of token n inside V^T: bits 2 and 3 of n swapped, so that within every 16-token
-// group the 8 tokens {0..3, 8..11} come first and {4..7, 12..15} second -- the 8 keys that
-// lane half 0 and lane half 1 feed into one PV K-step
-__host__ __device__ inline int64_t vt_pos(int64_t n) { return (n & ~int64_t(12)) | ((n & 4) << 1) | ((n & 8) >> 1); }
 
 __device__ inline void wait_vmcnt_le(int n) {
     // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt at their maxima)
@@ -970,91 +970,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-// V [N][Hkv][D] (bf16 or fp32, rounded to bf16) -> V^T tiles [Hkv][G][D][64] (each 64-token tile's
-// D rows of 128 bytes contiguous, so that the attention's tile loads cover one 16 KB block) with
-// the tokens of every 16-token group at vt_pos.  One workgroup per (64-token tile, kv head): the tile goes through
-// LDS so that both the 2D-byte row reads and the 128-byte V^T row writes are whole rows.
-template <int D, typename T>
-__global__ __launch_bounds__(256) void transpose_v_kernel(const T *__restrict__ v, uint16_t *__restrict__ vt,
-                                                          int Hkv, int64_t N, int *__restrict__ header) {
-    // the attention kernel that follows on the stream claims rows from the counters and raises
-    // flags in the status word: both start at zero for every call
-    if (blockIdx.x == 0 && blockIdx.y == 0) {
-        if (threadIdx.x < kXcds) header[threadIdx.x] = 0;
-        if (threadIdx.x == 64) header[kStatusWord] = 0;
-    }
-    constexpr int LD = D + 2;  // padded LDS row (bf16 elements): column reads hit distinct banks
-    constexpr int CH = D / 8;  // 8-element chunks per token row
-    __shared__ uint16_t tile[64 * LD];
-    const int t = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
-    const int64_t tok0 = static_cast<int64_t>(t) * kTile;
-    // read: 8 consecutive elements (16 or 32 bytes) of one token row per thread and pass
-    for (int x = tid; x < 64 * CH; x += 256) {
-        const int r = x / CH, c = x % CH;
-        const T *src = v + ((tok0 + r) * Hkv + kvh) * D + 8 * c;
-        uint16_t *dst = tile + r * LD + 8 * c;
-        if constexpr (sizeof(T) == 2) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(src);
-            const uint32_t p[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                dst[2 * j] = static_cast<uint16_t>(p[j] & 0xFFFFu);
-                dst[2 * j + 1] = static_cast<uint16_t>(p[j] >> 16);
-            }
-        } else {
-            const float4 a = *reinterpret_cast<const float4 *>(src);
-            const float4 b = *reinterpret_cast<const float4 *>(src + 4);
-            const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) dst[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(f[j]));
-        }
-    }
-    __syncthreads();
-    // V^T row d of this tile: 64 stored positions; thread writes 8 consecutive positions
-    for (int x = tid; x < D * 8; x += 256) {
-        const int d = x / 8, c = x % 8;
-        uint16_t w[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) w[j] = tile[static_cast<int>(vt_pos(8 * c + j)) * LD + d];
-        uint4 pk;
-        pk.x = w[0] | (uint32_t(w[1]) << 16);
-        pk.y = w[2] | (uint32_t(w[3]) << 16);
-        pk.z = w[4] | (uint32_t(w[5]) << 16);
-        pk.w = w[6] | (uint32_t(w[7]) << 16);
-        *reinterpret_cast<uint4 *>(vt + ((static_cast<int64_t>(kvh) * (N / kTile) + t) * D + d) * kTile + 8 * c) = pk;
-    }
-}
-
-__global__ void cast_bf16_kernel(const float *__restrict__ src, __bf16 *__restrict__ dst, int64_t n) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
-        dst[i] = static_cast<__bf16>(src[i]);  // round to nearest even
-}
-
 }  // namespace
-
-hipError_t launch_cast_bf16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream) {
-    if (n <= 0) return hipSuccess;
-    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
-    cast_bf16_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(
-        src, reinterpret_cast<__bf16 *>(dst), n);
-    return hipGetLastError();
-}
-
-hipError_t launch_transpose_v(const HostLayout &hl, const void *v, bool fp32, uint16_t *vt, int *header,
-                              hipStream_t stream) {
-    if (hl.G == 0) return hipSuccess;
-    const int64_t N = int64_t(hl.G) * kTile;
-    const dim3 grid(static_cast<unsigned>(hl.G), static_cast<unsigned>(hl.Hkv));
-    if (hl.D == 128) {
-        if (fp32) transpose_v_kernel<128, float><<<grid, 256, 0, stream>>>(static_cast<const float *>(v), vt, hl.Hkv, N, header);
-        else transpose_v_kernel<128, __bf16><<<grid, 256, 0, stream>>>(static_cast<const __bf16 *>(v), vt, hl.Hkv, N, header);
-    } else {
-        if (fp32) transpose_v_kernel<64, float><<<grid, 256, 0, stream>>>(static_cast<const float *>(v), vt, hl.Hkv, N, header);
-        else transpose_v_kernel<64, __bf16><<<grid, 256, 0, stream>>>(static_cast<const __bf16 *>(v), vt, hl.Hkv, N, header);
-    }
-    return hipGetLastError();
-}
 
 hipError_t launch_prefill(const HostLayout &hl, const PlanView &pv, const uint16_t *q,
                           const uint16_t *k, const uint16_t *vt, const int32_t *row_ptr,

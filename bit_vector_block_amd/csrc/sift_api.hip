@@ -448,8 +448,8 @@ sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_pl
     int32_t *ca_prefix = reinterpret_cast<int32_t *>(tb);
     int32_t *ca_list = reinterpret_cast<int32_t *>(tb + align256(4 * size_t(hl.Hq) * size_t(hl.ndocs > 0 ? hl.ndocs : 1)));
     int32_t *rowinfo = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ca_list) + align256(4 * rows));
-    if (launch_bits_prepass(hl, pv, d_la, d_ca, ca_prefix, ca_list, rowinfo, stream) != hipSuccess ||
-        launch_transpose_v(hl, d_v, dtype == SIFT_FP32, vt, header, stream) != hipSuccess ||
+    if (launch_fused_prep(hl, pv, d_la, d_ca, ca_prefix, ca_list, rowinfo, d_v, dtype == SIFT_FP32, vt, header,
+                          stream) != hipSuccess ||
         launch_prefill(hl, pv, q, k, vt, nullptr, nullptr, 0, rowinfo, ca_list, d_la, scale, d_out, d_lse,
                        header, stream) != hipSuccess)
         return SIFT_ERR_HIP;

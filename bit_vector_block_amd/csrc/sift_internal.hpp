@@ -12,6 +12,7 @@
 namespace sift {
 
 constexpr int kTile = 64;
+constexpr int kPrefillQueues = 8;  // row-queue counters (one per XCD) at the start of the workspace
 constexpr uint32_t kPlanMagic = 0x54464953u;  // "SIFT"
 constexpr int kHeaderWords = 16;
 
@@ -73,9 +74,11 @@ size_t decode_workspace_bytes(const HostLayout &hl);
 hipError_t launch_decode(const HostLayout &hl, const PlanView &pv, const uint32_t *la,
                          const uint32_t *ca, int32_t *row_ptr, int32_t *col_idx, void *scratch,
                          int32_t *status, hipStream_t stream);
-// Fused path (no CSR): per head, the request-level CA page lists and per-row list records.
-hipError_t launch_bits_prepass(const HostLayout &hl, const PlanView &pv, const uint32_t *la, const uint32_t *ca,
-                               int32_t *ca_prefix, int32_t *ca_list, int32_t *rowinfo, hipStream_t stream);
+// Fused path (no CSR), one launch: per head, the request-level CA page lists and per-row list
+// records; and the V^T transpose with the header cleared, as launch_transpose_v.
+hipError_t launch_fused_prep(const HostLayout &hl, const PlanView &pv, const uint32_t *la, const uint32_t *ca,
+                             int32_t *ca_prefix, int32_t *ca_list, int32_t *rowinfo, const void *v, bool fp32,
+                             uint16_t *vt, int *header, hipStream_t stream);
 // Offline encoder (tile masses of dense attention, then top-p selection into LA/CA words).
 // `status` (may be null): the caller's device word for the sift_device_flag bits.
 // The tile-mass kernel is persistent: each workgroup claims work items from its XCD's queue
