@@ -360,20 +360,41 @@ def main(argv=None):
         # the same layer with the decode fused into the attention (sift_sparse_prefill_bits: a
         # per-head pre-pass of CA page lists, then lists built from the bits inside the kernel)
         log("fused decode-in-attention")
+
+        def fused_call():
+            sift.sparse_prefill_bits(lay, la, ca, q, k, v, plan=plan, workspace=ws, out=out)
+
+        def csr_step():
+            sift.decode_bits(lay, la, ca, plan=plan, workspace=ws, row_ptr=row_ptr, col_idx=col_idx)
+            sift.sparse_prefill(lay, q, k, v, row_ptr, col_idx, plan=plan, workspace=ws, out=out)
+
+        def run(fn, n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
         for _ in range(max(args.warmup, 1)):
-            sift.sparse_prefill_bits(lay, la, ca, q, k, v, plan=plan, workspace=ws, out=out)
+            fused_call()
         torch.cuda.synchronize()
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        f0.record(stream)
-        for _ in range(args.steps):
-            sift.sparse_prefill_bits(lay, la, ca, q, k, v, plan=plan, workspace=ws, out=out)
-        f1.record(stream)
-        torch.cuda.synchronize()
-        ms_f = f0.elapsed_time(f1) / args.steps
+        # the two paths in alternating rounds, so that both see the same clocks (a GPU held busy
+        # for long stretches changes its clock), and the ratio taken round by round
+        n_round = max(args.steps // 5, 2)
+        fused_ms, ratios = [], []
+        for _ in range(5):
+            f = run(fused_call, n_round)
+            c = run(csr_step, n_round)
+            fused_ms.append(f)
+            ratios.append(f / c)
+        ms_f = float(np.median(fused_ms))
         result["fused_decode"] = {
             "ms_per_layer": round(ms_f, 5),
             "tflops": round(flops / (ms_f * 1e-3) / 1e12, 3),
-            "vs_decode_plus_prefill": round(ms_f / ms_per_step, 3),
+            "vs_decode_plus_prefill": round(float(np.median(ratios)), 3),
+            "note": "median over 5 alternating rounds of fused calls and decode + CSR prefill steps",
         }
     if args.layers > 0:
         # a stack of layers: every layer's LA/CA bits differ (drawn at the workload's densities) and
