@@ -21,9 +21,10 @@ __device__ inline int popcount_range(const uint32_t *vec, int lo, int hi) {
     return cnt;
 }
 
-// Exclusive scan of one int per thread over a workgroup of kCountThreads threads (wave scans, then
-// the wave totals through sh[kCountThreads / 64]); total gets the workgroup's sum.  Every thread
-// of the workgroup calls it.
+// Exclusive scan of one int per thread over a workgroup of NT threads (wave scans, then the wave
+// totals through sh[NT / 64]); total gets the workgroup's sum.  Every thread of the workgroup
+// calls it.
+template <int NT = kCountThreads>
 __device__ inline int block_excl_scan(int x, int *sh, int &total) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int incl = x;
@@ -36,7 +37,7 @@ __device__ inline int block_excl_scan(int x, int *sh, int &total) {
     __syncthreads();
     int below = 0, all = 0;
 #pragma unroll
-    for (int w = 0; w < kCountThreads / 64; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
         const int v = sh[w];
         below += w < wave ? v : 0;
         all += v;

@@ -197,6 +197,7 @@ struct WaveState {
     bf16x8 qf[D / 16];
     f32x16 acc_o[D / 32];
     float m_run, l_run;
+    float thr;  // m_run + the lazy margin (raw score units): a raise is due when a score exceeds it
 };
 
 // Per-row constants a pipeline step needs.
@@ -253,26 +254,30 @@ __device__ __forceinline__ void apply_mask(f32x16 &s, int t, int kv_valid, const
     }
 }
 
-// Raise the reference max when the tile's max mt exceeds it by more than kLazyLog2 (decided
-// wave-uniformly), rescaling O and l; returns the exp2 bias -m * scale_log2.
+// Raise the reference max when a score of the tile exceeds it by more than kLazyLog2 (decided
+// wave-uniformly from each lane's own 16 scores: the two lanes of a query share m_run, so some
+// lane of the wave exceeds thr exactly when the query's tile max does), rescaling O and l, and
+// update the exp2 bias nbias = -m * scale_log2.  Only a raise needs the query's tile max.
 template <int D>
-__device__ __forceinline__ float lazy_raise(WaveState<D> &st, float mt, const RowCtx &c) {
-    if (__ballot(mt > st.m_run + c.lazy_raw) != 0) {
-        const float m_new = fmaxf(st.m_run, mt);
+__device__ __forceinline__ void lazy_raise(WaveState<D> &st, float lmax, float &nbias, const RowCtx &c) {
+    if (__ballot(lmax > st.thr) != 0) {
+        const float m_new = fmaxf(st.m_run, pair_max(lmax));
         // m_run = -inf gives exp2(-inf) = 0; both -inf leaves alpha = 1 (O and l are still 0)
         const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f((st.m_run - m_new) * c.scale_log2);
         st.m_run = m_new;
+        st.thr = m_new + c.lazy_raw;
         st.l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) st.acc_o[db] *= alpha;
+        nbias = (m_new == -INFINITY) ? 0.0f : -m_new * c.scale_log2;
     }
-    return (st.m_run == -INFINITY) ? 0.0f : -st.m_run * c.scale_log2;
 }
 
-__device__ __forceinline__ float tile_max(const f32x16 &s) {
+// max of the lane's 16 scores
+__device__ __forceinline__ float lane_max(const f32x16 &s) {
     const float a = max3f(s[0], s[1], s[2]), b = max3f(s[3], s[4], s[5]), d = max3f(s[6], s[7], s[8]);
     const float e = max3f(a, s[9], s[10]), f = max3f(b, s[11], s[12]), h = max3f(d, s[13], s[14]);
-    return pair_max(max3f(e, f, max3f(h, s[15], s[15])));
+    return max3f(e, f, max3f(h, s[15], s[15]));
 }
 
 // Scores of one K tile (used once per row, for the first listed tile).
@@ -353,10 +358,15 @@ __device__ __forceinline__ void step_compute(WaveState<D> &st, const f32x16 &s_c
         pb[k >> 2][(2 * k) & 7] = pr[0];
         pb[k >> 2][((2 * k) & 7) + 1] = pr[1];
     };
+    // l += the rounded pair k (the l sums run in pair order, so l is the same sum whatever the
+    // MFMA placement)
+    auto sum_pair = [&](int k) {
+        const bf16x2 pr = {pb[k >> 2][(2 * k) & 7], pb[k >> 2][((2 * k) & 7) + 1]};
+        l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+    };
     float p0 = 0.0f, p1 = 0.0f;  // exponentials of the last pair computed, not yet rounded
-    // exponentials of pair k, the fma of pair k + 1, and pair k - 1 rounded into pb and summed
-    // into l (in pair order, so l is the same sum whatever the MFMA placement); pair 3 is rounded
-    // on its own, ahead of the PV MFMAs that read it, so pair 4 does not round it again
+    // exponentials of pair k, the fma of pair k + 1, and pair k - 1 rounded into pb; pair 3 is
+    // rounded on its own, ahead of the PV MFMAs that read it, so pair 4 does not round it again
     auto next_pair = [&](int k) {
         const float n0 = __builtin_amdgcn_exp2f(x0), n1 = __builtin_amdgcn_exp2f(x1);
         if (k < 7) {
@@ -395,10 +405,10 @@ __device__ __forceinline__ void step_compute(WaveState<D> &st, const f32x16 &s_c
         __builtin_amdgcn_sched_barrier(0);
     }
     round_pair(7, p0, p1);  // pb[1] complete
-    st.l_run = l;
     __builtin_amdgcn_sched_barrier(0);
-    // PV of pairs 4..7 (pb[1]: the odd K-steps), with the max tree of S(e+1) behind it (no branch
-    // inside this region: a branch would let the exponentials above sink past the barriers)
+    // PV of pairs 4..7 (pb[1]: the odd K-steps), with the l sums of all eight pairs and the max
+    // tree of S(e+1) behind it (no branch inside this region: a branch would let the
+    // exponentials above sink past the barriers)
     float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f;
 #pragma unroll
     for (int j = 0; j < DC / 2; ++j) {
@@ -416,12 +426,17 @@ __device__ __forceinline__ void step_compute(WaveState<D> &st, const f32x16 &s_c
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    float mt = pair_max(max3f(m0, m1, max3f(m2, s[15], s[15])));
+    float mt = max3f(m0, m1, max3f(m2, s[15], s[15]));
+    // both results taken here, ahead of the mask branch: otherwise the compiler sinks the l sums
+    // (rebuilding packed words whose registers it reused) and merges this max tree with the
+    // masked one, out of the MFMA region
+    asm volatile("" : "+v"(mt));
+    st.l_run = l;
     if (needs_mask(t_next, v_next, c)) {  // diagonal or partial tile: mask, then max again
         apply_mask(s, t_next, v_next, c);
-        mt = tile_max(s);
+        mt = lane_max(s);
     }
-    nbias = lazy_raise<D>(st, mt, c);
+    lazy_raise<D>(st, mt, nbias, c);
     s_nxt = s;
 }
 
@@ -800,6 +815,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int db = 0; db < DB; ++db) st.acc_o[db] = f32x16{};
         st.m_run = -INFINITY;
         st.l_run = 0.0f;
+        st.thr = -INFINITY;
 
         // the next row: its claim went out one row ago and resolves at this row's first barrier,
         // when the claim for the row after it goes out
@@ -865,7 +881,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             resolve_next();  // the prologue barrier
             sa = qk_tile<D>(st, kb0, ctx);
             if (needs_mask(t0, v0, ctx)) apply_mask(sa, t0, v0, ctx);
-            nbias = lazy_raise<D>(st, tile_max(sa), ctx);
+            lazy_raise<D>(st, lane_max(sa), nbias, ctx);
             // steady state, unrolled by two so that every buffer and score register has a fixed
             // role: step e: wait + barrier; K(e+2) -> free K buffer, V(e+1) -> free V buffer; compute
             int t_a = t1, v_a = v1;  // entry i + 1

@@ -12,7 +12,6 @@ namespace sift {
 
 namespace {
 
-constexpr int32_t kPlanVersion = 1;
 constexpr int64_t kInt32Max = 2147483647LL;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -96,7 +95,7 @@ sift_status build_layout(const sift_layout *layout, HostLayout *out) {
     // plan image
     const int64_t nd = ndocs, R = L.num_requests;
     std::vector<int32_t> &p = hl.plan;
-    p.assign(kHeaderWords + 3 * G + 7 * nd + 3 * R, 0);
+    p.assign(kHeaderWords + 3 * G + 7 * nd + 3 * R + kRecWords * (G + nd), 0);
     int32_t *hdr = p.data();
     hdr[0] = static_cast<int32_t>(kPlanMagic);
     hdr[1] = kPlanVersion;
@@ -119,6 +118,8 @@ sift_status build_layout(const sift_layout *layout, HostLayout *out) {
     int32_t *req_first = doc_req + nd;
     int32_t *req_first_doc = req_first + R;
     int32_t *req_ndocs = req_first_doc + R;
+    int32_t *tile_rec = req_ndocs + R;
+    int32_t *doc_rec = tile_rec + kRecWords * G;
     int64_t g = 0, d = 0, la_acc = 0, ca_acc = 0;
     for (int32_t b = 0; b < L.num_requests; ++b) {
         req_first[b] = static_cast<int32_t>(g);
@@ -136,18 +137,42 @@ sift_status build_layout(const sift_layout *layout, HostLayout *out) {
             doc_ca_off[d] = static_cast<int32_t>(ca_acc);
             la_acc += static_cast<int64_t>(L.num_q_heads) * doc_la_w[d];
             ca_acc += static_cast<int64_t>(L.num_q_heads) * doc_ca_w[d];
+            int32_t *dr = doc_rec + kRecWords * d;
+            dr[kDrCaOff] = doc_ca_off[d];
+            dr[kDrCaW] = doc_ca_w[d];
+            dr[kDrTiles] = doc_tiles[d];
+            dr[kDrReqDoc] = req_first_doc[b];
+            dr[kDrFirst] = doc_first[d];
+            dr[kDrReq] = req_first[b];
+            dr[kDrLaOff] = doc_la_off[d];
             for (int64_t r = 0; r < T; ++r, ++g) {
                 tile_doc[g] = static_cast<int32_t>(d);
                 tile_local[g] = static_cast<int32_t>(r);
                 tile_valid[g] = static_cast<int32_t>(std::min<int64_t>(kTile, n - r * kTile));
+                int32_t *tr = tile_rec + kRecWords * g;
+                tr[kTrDoc] = static_cast<int32_t>(d);
+                tr[kTrLocal] = static_cast<int32_t>(r);
+                tr[kTrFirst] = doc_first[d];
+                tr[kTrReq] = req_first[b];
+                tr[kTrLaOff] = doc_la_off[d];
+                tr[kTrLaW] = doc_la_w[d];
+                tr[kTrLo] = static_cast<int32_t>(r * (r + 1) / 2);
             }
         }
+        for (int64_t e = req_first_doc[b]; e < d; ++e)  // g is now the request's first question tile
+            doc_rec[kRecWords * e + kDrAfter] = static_cast<int32_t>(g - (doc_first[e] + doc_tiles[e]));
         const int64_t m = L.question_len[b];
         const int64_t TQ = ceil_div(m, kTile);
         for (int64_t r = 0; r < TQ; ++r, ++g) {
+            hl.question_nnz += g - req_first[b] + 1;
             tile_doc[g] = -(b + 1);
             tile_local[g] = static_cast<int32_t>(r);
             tile_valid[g] = static_cast<int32_t>(std::min<int64_t>(kTile, m - r * kTile));
+            int32_t *tr = tile_rec + kRecWords * g;
+            tr[kTrDoc] = -(b + 1);
+            tr[kTrLocal] = static_cast<int32_t>(r);
+            tr[kTrFirst] = req_first[b];
+            tr[kTrReq] = req_first[b];
         }
     }
     *out = std::move(hl);
@@ -172,6 +197,8 @@ PlanView plan_view(const HostLayout &hl, const void *d_plan) {
     v.req_first = v.doc_req + nd;
     v.req_first_doc = v.req_first + R;
     v.req_ndocs = v.req_first_doc + R;
+    v.tile_rec = v.req_ndocs + R;
+    v.doc_rec = v.tile_rec + kRecWords * G;
     v.fp_lo = static_cast<uint32_t>(hl.fingerprint & 0xffffffffu);
     v.fp_hi = static_cast<uint32_t>(hl.fingerprint >> 32);
     v.num_requests = hl.R;

@@ -15,6 +15,7 @@ constexpr int kTile = 64;
 constexpr int kPrefillQueues = 8;  // row-queue counters (one per XCD) at the start of the workspace
 constexpr uint32_t kPlanMagic = 0x54464953u;  // "SIFT"
 constexpr int kHeaderWords = 16;
+constexpr int32_t kPlanVersion = 2;  // header word 1: the plan image's format
 
 // Every workspace starts with a 256-byte header: int32 words 0..7 are the attention kernel's
 // row-queue counters, word kStatusWord holds the sift_device_flag bits of the last call that
@@ -38,14 +39,41 @@ struct PlanView {
     const int32_t *req_first;   // [R]: global first tile of the request
     const int32_t *req_first_doc;  // [R]: global index of the request's first document
     const int32_t *req_ndocs;   // [R]
+    // The same facts gathered per tile and per document (kRecWords int32 each), so that a
+    // kernel gets all of a row's or a document's fields in one round trip to memory:
+    const int32_t *tile_rec;    // [G][8]: TileRec fields
+    const int32_t *doc_rec;     // [Ndocs][8]: DocRec fields
     uint32_t fp_lo, fp_hi;      // fingerprint the host expects
     int32_t num_requests, num_docs, num_tiles, num_q_heads;
 };
 
+constexpr int kRecWords = 8;
+// tile_rec[g]: the segment of tile g and where its row's bits and list parts live.
+enum TileRec {
+    kTrDoc = 0,    // global document, or -(b + 1) for a question tile of request b
+    kTrLocal = 1,  // r: index of the tile in its segment
+    kTrFirst = 2,  // first tile of the document (of the request, for a question tile)
+    kTrReq = 3,    // first tile of the request
+    kTrLaOff = 4,  // word offset of the document's (head 0) LA vector (0 for a question tile)
+    kTrLaW = 5,    // words per (document, head) LA vector (0 for a question tile)
+    kTrLo = 6,     // first LA bit of the row: r (r + 1) / 2 (0 for a question tile)
+};
+// doc_rec[d]
+enum DocRec {
+    kDrCaOff = 0,  // word offset of the document's (head 0) CA vector
+    kDrCaW = 1,    // words per (document, head) CA vector
+    kDrTiles = 2,  // T_d
+    kDrReqDoc = 3, // first document of the request
+    kDrFirst = 4,  // first tile of the document
+    kDrReq = 5,    // first tile of the request
+    kDrLaOff = 6,  // word offset of the document's (head 0) LA vector
+    kDrAfter = 7,  // tiles of the later documents of the request
+};
+
 // Device check that an uploaded plan belongs to the layout the host validated: the plan header's
-// magic, fingerprint and tile count against the host's values carried in `pv`.
+// magic, format, fingerprint and tile count against the host's values carried in `pv`.
 __device__ inline bool plan_ok(const PlanView &pv) {
-    return pv.header[0] == static_cast<int32_t>(kPlanMagic) &&
+    return pv.header[0] == static_cast<int32_t>(kPlanMagic) && pv.header[1] == kPlanVersion &&
            static_cast<uint32_t>(pv.header[2]) == pv.fp_lo &&
            static_cast<uint32_t>(pv.header[3]) == pv.fp_hi && pv.header[6] == pv.num_tiles;
 }
@@ -56,6 +84,7 @@ struct HostLayout {
     int64_t la_words = 0, ca_words = 0, max_nnz = 0;
     int64_t max_doc_tiles = 0;
     int64_t max_req_tiles = 0;
+    int64_t question_nnz = 0;  // list entries of one head's question rows (the same for every head)
     uint64_t fingerprint = 0;
     std::vector<int32_t> plan;  // the full plan image (header + arrays)
 };

@@ -137,11 +137,13 @@ size_t sift_workspace_bytes(const sift_layout *layout, sift_dtype dtype);
 
 /*
  * sift_plan_upload: write the layout's device tables (per-tile segment data,
- * per-document bit offsets, per-request first tiles) into d_plan, a caller
- * buffer of at least sift_plan_bytes() bytes, with one hipMemcpyAsync on
- * `stream` from a host staging copy.  A plan depends on the layout only, so one
- * upload serves every layer of a batch.  The plan carries a fingerprint of the
- * layout; a kernel launched with a plan of another layout computes nothing and
+ * per-document bit offsets, per-request first tiles, and the same facts gathered
+ * into one record per tile and per document) into d_plan, a caller buffer of at
+ * least sift_plan_bytes() bytes, with one hipMemcpyAsync on `stream` from a host
+ * staging copy.  A plan depends on the layout only, so one upload serves every
+ * layer of a batch.  The plan carries a fingerprint of the layout and its format
+ * version; a kernel launched with a plan of another layout (or of another version
+ * of this library) computes nothing and
  * raises SIFT_DEVICE_PLAN_MISMATCH in the call's device status word (the host
  * cannot see the plan's contents without a synchronisation).
  * Errors: SIFT_ERR_INVALID (layout, null), SIFT_ERR_CAPACITY (plan_bytes),

@@ -99,3 +99,20 @@ def test_decode_empty_layout():
     case = W.make_case("empty", 10, [0], [], [0], 2, 1, 64, np.zeros((1, 2)), np.zeros((1, 2)))
     rp, ci = gpu_decode(case)
     assert rp.tolist() == [0] and ci.size == 0
+
+
+# Layouts at and past the single-launch decode's per-head LDS bounds (2048 rows, 1024 documents,
+# 64 tiles per document); past them the decode runs as two launches.
+@pytest.mark.parametrize("name,req_num_docs,doc_tiles,question_len", [
+    ("at_bounds", [1024], [2] * 1024, [0]),               # G 2048, 1024 documents
+    ("rows_past_bound", [33], [64] * 33, [70]),           # G 2114
+    ("docs_past_bound", [515, 515], [1] * 1030, [64, 1]),  # 1030 documents
+    ("doc_tiles_past_bound", [2], [65, 3], [10]),         # a 65-tile document
+])
+def test_decode_single_launch_bounds(name, req_num_docs, doc_tiles, question_len):
+    doc_len = [64 * t - (i % 7) for i, t in enumerate(doc_tiles)]
+    r = len(req_num_docs)
+    case = W.make_case(name, 11, req_num_docs, doc_len, question_len, 1, 1, 64,
+                       np.full((r, 1), 0.3), np.full((r, 1), 0.2))
+    print(f"decode {name}: G={case.q.shape[0] // 64} docs={len(doc_len)}", flush=True)
+    _check(case)
