@@ -487,74 +487,26 @@ __device__ __forceinline__ void list_entry(const TileList &L, int i, int &t, int
     valid = p < 0 ? 0 : (p >> 25) + 1;
 }
 
-struct RowMeta;
-template <bool FUSED>
-__device__ __forceinline__ int chunk_ids(int base, const RowMeta &m, const int32_t *__restrict__ col_idx,
-                                         const int32_t *__restrict__ ca_list, const uint32_t *__restrict__ la,
-                                         int lane);
-
-template <bool FUSED>
-__device__ __forceinline__ RowMeta meta_of(int w);
-
-template <bool FUSED>
-__device__ __forceinline__ void advance_chunk(TileList &L, int i, int mw, int G,
-                                              const int32_t *__restrict__ col_idx,
-                                              const int32_t *__restrict__ ca_list, const uint32_t *__restrict__ la,
-                                              const int32_t *__restrict__ tile_valid, int lane, int *status) {
-    if ((i >> 6) != L.c) {  // entry i entered chunk c + 1: shift, fetch chunk c + 2's ids
-        L.c += 1;
-        L.c0 = L.c1;
-        L.c1 = chunk_ids<FUSED>(64 * (L.c + 1), meta_of<FUSED>(mw), col_idx, ca_list, la, lane);
-        L.raw1 = true;
-    } else if (L.raw1) {  // one step later: their valid counts
-        L.c1 = with_valid(L.c1, G, tile_valid, status);
-        L.raw1 = false;
-    }
-}
-
-// Where a row's list comes from.  CSR path: row_ptr / col_idx written by the decode kernel.
-// Fused path (no CSR): the row's record from the pre-pass (its CA entries are a slice of its
-// request's CA page list, its LA entries are the set bits of its own LA row, read here).
+// A row's list in the CSR: its entries are col_idx[e0 .. e0 + n).
 struct RowMeta {
-    int n;        // entries
-    int e0;       // CSR: the row's first entry in col_idx
-    int ca_n;     // fused: CA entries (-1: question row, tiles t0 .. t0 + n - 1)
-    int ca_base;  // fused: the row's CA entries start at ca_list[ca_base]
-    int la_word;  // fused: word offset of the row's (document, head) LA vector
-    int la_lo;    // fused: first bit of the row in that vector
-    int t0;       // fused: first tile of the document (or of the request, for a question row)
-    int r;        // fused: the row's LA bits are [la_lo, la_lo + r]
+    int n;   // entries
+    int e0;  // the row's first entry in col_idx
 };
 
-// The word(s) a row's metadata is read from: lanes 0, 1 get row_ptr[row], row_ptr[row + 1];
-// lanes 0..7 get the row's 8-int record.
-template <bool FUSED>
-__device__ __forceinline__ int meta_word(int64_t row, const int32_t *__restrict__ row_ptr,
-                                         const int32_t *__restrict__ rowinfo, int lane) {
-    if constexpr (FUSED) return rowinfo[row * 8 + (lane & 7)];
-    else return row_ptr[row + (lane & 1)];
+// The word a row's metadata is read from: lanes 0, 1 get row_ptr[row], row_ptr[row + 1].
+__device__ __forceinline__ int meta_word(int64_t row, const int32_t *__restrict__ row_ptr, int lane) {
+    return row_ptr[row + (lane & 1)];
 }
 
-template <bool FUSED>
 __device__ __forceinline__ RowMeta meta_of(int w) {
-    RowMeta m{};
-    if constexpr (FUSED) {
-        m.n = __builtin_amdgcn_readlane(w, 0);
-        m.ca_n = __builtin_amdgcn_readlane(w, 1);
-        m.ca_base = __builtin_amdgcn_readlane(w, 2);
-        m.la_word = __builtin_amdgcn_readlane(w, 3);
-        m.la_lo = __builtin_amdgcn_readlane(w, 4);
-        m.t0 = __builtin_amdgcn_readlane(w, 5);
-        m.r = __builtin_amdgcn_readlane(w, 6);
-    } else {
-        m.e0 = __builtin_amdgcn_readlane(w, 0);
-        m.n = __builtin_amdgcn_readlane(w, 1) - m.e0;
-    }
+    RowMeta m;
+    m.e0 = __builtin_amdgcn_readlane(w, 0);
+    m.n = __builtin_amdgcn_readlane(w, 1) - m.e0;
     return m;
 }
 
-// CSR path: a row whose [row_ptr[r], row_ptr[r + 1]) is not inside [0, col_entries] is read as
-// empty and flagged in the status word, so no entry outside the caller's col_idx is read.
+// A row whose [row_ptr[r], row_ptr[r + 1]) is not inside [0, col_entries] is read as empty and
+// flagged in the status word, so no entry outside the caller's col_idx is read.
 __device__ __forceinline__ int checked_meta(int w, int64_t col_entries, int *status) {
     const int e0 = __builtin_amdgcn_readlane(w, 0), e1 = __builtin_amdgcn_readlane(w, 1);
     const bool ok = e0 >= 0 && e1 >= e0 && static_cast<int64_t>(e1) <= col_entries;  // uniform
@@ -562,69 +514,18 @@ __device__ __forceinline__ int checked_meta(int w, int64_t col_entries, int *sta
     return ok ? w : 0;
 }
 
-// Fused: lane j gets word j of the row's LA bit range (at most 64 words, checked on the host).
-__device__ __forceinline__ uint32_t load_la_words(const RowMeta &m, const uint32_t *__restrict__ la, int lane) {
-    if (m.ca_n < 0) return 0u;
-    const int w0 = m.la_lo >> 5, w1 = (m.la_lo + m.r) >> 5;
-    return (w0 + lane <= w1) ? la[m.la_word + w0 + lane] : 0u;
-}
-
-// Fused: raw tile ids of entries [base, base + 64) of a row (kNoEntry past its end); law =
-// load_la_words of the row.
-// A CA entry is a load from the request's page list (not waited for here); an LA entry is the
-// k-th set bit of the row's LA range, found from a prefix sum of the per-lane popcounts.
-__device__ __forceinline__ int gen_ids(int base, const RowMeta &m, uint32_t law, const int32_t *__restrict__ ca_list,
-                                       int lane) {
-    const int e = base + lane;
-    if (m.ca_n < 0) return e < m.n ? m.t0 + e : kNoEntry;  // question row: a dense range
-    const int w0 = m.la_lo >> 5, nw = ((m.la_lo + m.r) >> 5) - w0 + 1;
-    uint32_t x = lane < nw ? law : 0u;
-    if (lane == 0) x &= ~0u << (m.la_lo & 31);
-    if (lane == nw - 1) {
-        const int hb = (m.la_lo + m.r) & 31;
-        x &= (hb == 31) ? ~0u : ((2u << hb) - 1u);
+__device__ __forceinline__ void advance_chunk(TileList &L, int i, int mw, int G, const int32_t *__restrict__ col_idx,
+                                              const int32_t *__restrict__ tile_valid, int lane, int *status) {
+    if ((i >> 6) != L.c) {  // entry i entered chunk c + 1: shift, fetch chunk c + 2's ids
+        L.c += 1;
+        L.c0 = L.c1;
+        const RowMeta m = meta_of(mw);
+        L.c1 = load_ids(64 * (L.c + 1), m.n, m.e0, col_idx, lane);
+        L.raw1 = true;
+    } else if (L.raw1) {  // one step later: their valid counts
+        L.c1 = with_valid(L.c1, G, tile_valid, status);
+        L.raw1 = false;
     }
-    const int pc = __popc(x);
-    int S = pc;  // inclusive prefix over lanes
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(S, off, 64);
-        if (lane >= off) S += y;
-    }
-    const int k = e - m.ca_n;  // LA rank of this lane's entry (meaningful when >= 0)
-    int i = 0;                 // the first lane whose inclusive prefix exceeds k
-#pragma unroll
-    for (int step = 32; step > 0; step >>= 1) {
-        const int s_probe = __shfl(S, min(i + step - 1, 63), 64);
-        if (s_probe <= k) i += step;
-    }
-    const int ic = min(i, 63);
-    uint32_t word = static_cast<uint32_t>(__shfl(static_cast<int>(x), ic, 64));
-    int rem = k - (__shfl(S, ic, 64) - __shfl(pc, ic, 64));
-    int pos = 0;
-#pragma unroll
-    for (int width = 16; width > 0; width >>= 1) {  // the rem-th set bit of word
-        const int c = __popc(word & ((1u << width) - 1u));
-        if (rem >= c) {
-            rem -= c;
-            word >>= width;
-            pos += width;
-        }
-    }
-    int t = (e < m.n) ? m.t0 + (32 * (w0 + ic) + pos - m.la_lo) : kNoEntry;
-    if (e < m.ca_n) t = ca_list[m.ca_base + e];
-    return t;
-}
-
-// Raw tile ids of entries [base, base + 64): CSR loads, or (fused) generated from the bits (this
-// reads the row's LA words and waits for them; used at the start of a row's list and at its
-// 64-entry boundaries).
-template <bool FUSED>
-__device__ __forceinline__ int chunk_ids(int base, const RowMeta &m, const int32_t *__restrict__ col_idx,
-                                         const int32_t *__restrict__ ca_list, const uint32_t *__restrict__ la,
-                                         int lane) {
-    if constexpr (FUSED) return gen_ids(base, m, load_la_words(m, la, lane), ca_list, lane);
-    else return load_ids(base, m.n, m.e0, col_idx, lane);
 }
 
 // A zero the compiler cannot see through: per-row values derived from it are recomputed for
@@ -739,12 +640,11 @@ __device__ __forceinline__ void finish_half(const WaveState<D> &st, const f32x4 
 // known to every wave by row r's first barrier; its CSR offsets load during row r's first
 // tile, its tile ids during the second, its Q during the last, and its first K and V^T tiles
 // stream in while row r's two key halves are merged and stored.
-template <int D, bool FUSED>
+template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_prefill_kernel(
     PlanView pv, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ vt, const int32_t *__restrict__ row_ptr,
-    const int32_t *__restrict__ col_idx, const int32_t *__restrict__ rowinfo,
-    const int32_t *__restrict__ ca_list, const uint32_t *__restrict__ la_bits, int64_t col_entries, float scale,
+    const int32_t *__restrict__ col_idx, int64_t col_entries, float scale,
     float scale_log2, float lazy_raw, float *__restrict__ out, float *__restrict__ lse, int Hq, int Hkv, Queues Qs,
     int *__restrict__ counters) {
     using C = Cfg<D>;
@@ -794,11 +694,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     RowId rid = row_of(row_idx, G, group);
     WaveState<D> st;
     load_q<D>(st, q, rid, Hq, qi, hi);
-    int mw = meta_word<FUSED>(static_cast<int64_t>(rid.h) * G + rid.g, row_ptr, rowinfo, lane);
-    if constexpr (!FUSED) mw = checked_meta(mw, col_entries, status);
-    int n = meta_of<FUSED>(mw).n;
+    int mw = checked_meta(meta_word(static_cast<int64_t>(rid.h) * G + rid.g, row_ptr, lane), col_entries, status);
+    int n = meta_of(mw).n;
     // raw tile ids of the row's entries 0..63
-    int ids0 = chunk_ids<FUSED>(0, meta_of<FUSED>(mw), col_idx, ca_list, la_bits, lane);
+    int ids0 = load_ids(0, n, meta_of(mw).e0, col_idx, lane);
     bool first_issued = false;  // K(0) -> kb0 and V(0) -> vb0 already in flight
 
     while (true) {
@@ -821,8 +720,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // when the claim for the row after it goes out
         int next_idx = -1;
         int nmw = 0;      // the next row's metadata word
-        int nids = -1;    // stage 2: raw tile ids of the next row's entries 0..63 (stage 1, fused: its LA words)
-        int nstage = 0;   // 0: nothing fetched, 1: (fused) LA words in flight, 2: ids in flight
+        int nids = -1;    // raw tile ids of the next row's entries 0..63, once fetched
+        bool nfetched = false;
         auto resolve_next = [&]() {  // every wave; includes a workgroup barrier
             const int slot = claim_no & 1;
             if (claimer) {
@@ -835,26 +734,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             ++claim_no;
             if (next_idx >= 0) {
                 const RowId nid = row_of(next_idx, G, group);
-                nmw = meta_word<FUSED>(static_cast<int64_t>(nid.h) * G + nid.g, row_ptr, rowinfo, lane);
+                nmw = meta_word(static_cast<int64_t>(nid.h) * G + nid.g, row_ptr, lane);
             }
         };
-        // one stage per call: the next row's metadata landed -> (fused) its LA words -> its tile ids
+        // the next row's metadata landed -> its tile ids
         auto fetch_next_ids = [&]() {
-            if (next_idx < 0 || nstage == 2) return;
-            const RowMeta nm = meta_of<FUSED>(nmw);
-            if constexpr (FUSED) {
-                if (nstage == 0) {
-                    nids = static_cast<int>(load_la_words(nm, la_bits, lane));
-                    nstage = 1;
-                    return;
-                }
-                nids = gen_ids(0, nm, static_cast<uint32_t>(nids), ca_list, lane);
-            } else {
-                nmw = checked_meta(nmw, col_entries, status);  // before any col_idx read of the row
-                const RowMeta cm = meta_of<FUSED>(nmw);
-                nids = load_ids(0, cm.n, cm.e0, col_idx, lane);
-            }
-            nstage = 2;
+            if (next_idx < 0 || nfetched) return;
+            nmw = checked_meta(nmw, col_entries, status);  // before any col_idx read of the row
+            const RowMeta nm = meta_of(nmw);
+            nids = load_ids(0, nm.n, nm.e0, col_idx, lane);
+            nfetched = true;
         };
 
         int i = 0;
@@ -872,7 +761,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             TileList L;
             L.c = 0;
             L.c0 = with_valid(ids0, G, pv.tile_valid, status);
-            L.c1 = n > 64 ? chunk_ids<FUSED>(64, meta_of<FUSED>(mw), col_idx, ca_list, la_bits, lane) : -1;
+            L.c1 = n > 64 ? load_ids(64, n, meta_of(mw).e0, col_idx, lane) : -1;
             L.raw1 = n > 64;
             int t0, v0, t1, v1;
             list_entry(L, 0, t0, v0);
@@ -886,7 +775,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // role: step e: wait + barrier; K(e+2) -> free K buffer, V(e+1) -> free V buffer; compute
             int t_a = t1, v_a = v1;  // entry i + 1
             while (i + 1 < n) {
-                advance_chunk<FUSED>(L, i, mw, G, col_idx, ca_list, la_bits, pv.tile_valid, lane, status);
+                advance_chunk(L, i, mw, G, col_idx, pv.tile_valid, lane, status);
                 int t_b, v_b;
                 list_entry(L, i + 2, t_b, v_b);
                 wait_vmcnt_le(0);
@@ -900,13 +789,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 t_a = t_b;
                 v_a = v_b;
                 if (i + 1 >= n) break;
-                advance_chunk<FUSED>(L, i, mw, G, col_idx, ca_list, la_bits, pv.tile_valid, lane, status);
+                advance_chunk(L, i, mw, G, col_idx, pv.tile_valid, lane, status);
                 list_entry(L, i + 2, t_b, v_b);
                 wait_vmcnt_le(0);
                 __builtin_amdgcn_s_barrier();
                 if (i + 2 < n) load_k_tile<D>(k_tile_base<D>(ctx, t_b), kb1, wave, off.k);
                 load_vt_tile<D>(vt_tile_base<D>(ctx, t_a), vb0, wave, off.v);
-                if (FUSED && i == 1) fetch_next_ids();  // (fused) the next row's LA words landed
                 __builtin_amdgcn_sched_barrier(0);
                 step_compute<D>(st, sb, sa, nbias, kb0, vb1, t_a, v_a, ctx);
                 ++i;
@@ -920,7 +808,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         } else {
             resolve_next();
         }
-        fetch_next_ids();
         fetch_next_ids();
         if (next_idx >= 0) load_q<D>(st, q, row_of(next_idx, G, group), Hq, qi, hi);
         if (n > 0) {
@@ -948,7 +835,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const bool has_next = next_idx >= 0;
         int nn = 0;
         if (has_next) {
-            nn = meta_of<FUSED>(nmw).n;
+            nn = meta_of(nmw).n;
             if (nn > 0) {
                 const RowId nid = row_of(next_idx, G, group);
                 const int i0 = valid_id(__builtin_amdgcn_readlane(nids, 0), G);
@@ -990,10 +877,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 hipError_t launch_prefill(const HostLayout &hl, const PlanView &pv, const uint16_t *q,
                           const uint16_t *k, const uint16_t *vt, const int32_t *row_ptr,
-                          const int32_t *col_idx, int64_t col_entries, const int32_t *rowinfo,
-                          const int32_t *ca_list, const uint32_t *la_bits, float scale, float *out, float *lse,
+                          const int32_t *col_idx, int64_t col_entries, float scale, float *out, float *lse,
                           int *header, hipStream_t stream) {
-    const bool fused = rowinfo != nullptr;
     const int64_t rows = int64_t(hl.Hq) * hl.G;
     if (rows == 0) return hipSuccess;
     const float scale_log2 = scale * 1.4426950408889634f;
@@ -1014,19 +899,14 @@ hipError_t launch_prefill(const HostLayout &hl, const PlanView &pv, const uint16
     // persistent: two workgroups per CU (256 CUs), never more workgroups than rows
     const int per_xcd = static_cast<int>(std::min<int64_t>((rows + kXcds - 1) / kXcds, kPersistentPerXcd));
     const unsigned grid = static_cast<unsigned>(per_xcd) * kXcds;
-#define SIFT_LAUNCH(DD, FF)                                                                              \
-    sparse_prefill_kernel<DD, FF><<<grid, kThreads, 0, stream>>>(pv, q, k, vt, row_ptr, col_idx, rowinfo,  \
-                                                                 ca_list, la_bits, col_entries, scale,   \
-                                                                 scale_log2, lazy_raw, out, lse, hl.Hq,  \
-                                                                 hl.Hkv, Qs, header)
-    if (hl.D == 128) {
-        if (fused) SIFT_LAUNCH(128, true);
-        else SIFT_LAUNCH(128, false);
-    } else {
-        if (fused) SIFT_LAUNCH(64, true);
-        else SIFT_LAUNCH(64, false);
-    }
-#undef SIFT_LAUNCH
+    if (hl.D == 128)
+        sparse_prefill_kernel<128><<<grid, kThreads, 0, stream>>>(pv, q, k, vt, row_ptr, col_idx, col_entries, scale,
+                                                                  scale_log2, lazy_raw, out, lse, hl.Hq, hl.Hkv, Qs,
+                                                                  header);
+    else
+        sparse_prefill_kernel<64><<<grid, kThreads, 0, stream>>>(pv, q, k, vt, row_ptr, col_idx, col_entries, scale,
+                                                                 scale_log2, lazy_raw, out, lse, hl.Hq, hl.Hkv, Qs,
+                                                                 header);
     return hipGetLastError();
 }
 

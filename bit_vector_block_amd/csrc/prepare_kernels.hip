@@ -1,12 +1,13 @@
 // Work that prepares the attention kernel's inputs (gfx950):
-//   transpose_v_kernel  V [N][Hkv][D] -> V^T tiles in the attention's layout (CSR path), and the
-//                       workspace header (row-queue counters, status word) cleared;
-//   fused_prep_kernel   the fused path's bits pre-pass (per q head: CA prefixes, CA page lists,
-//                       per-row list records) and the same transpose in one launch;
-//   cast_bf16_kernel    fp32 inputs rounded to bf16.
+//   transpose_v_kernel       V [N][Hkv][D] -> V^T tiles in the attention's layout, and the
+//                            workspace header (row-queue counters, status word) cleared;
+//   decode_transpose_kernel  the fused path's launch: the single-launch decode of the layer's
+//                            bits into a CSR of the workspace, beside the same transpose;
+//   cast_bf16_kernel         fp32 inputs rounded to bf16.
 #include <algorithm>
 
 #include "bits_common.hpp"
+#include "decode_one.hpp"
 #include "sift_internal.hpp"
 
 namespace sift {
@@ -20,67 +21,23 @@ using namespace bits;
 // lane half 0 and lane half 1 feed into one PV K-step
 __host__ __device__ inline int64_t vt_pos(int64_t n) { return (n & ~int64_t(12)) | ((n & 4) << 1) | ((n & 8) >> 1); }
 
-// Pre-pass of the fused path (no CSR), one workgroup of kCountThreads threads per q head h:
-//   ca_prefix[h][d] : CA entries of the earlier documents of d's request (request-local);
-//   ca_list[h][req_first[b] + k] : the k-th CA-marked page of request b, in document order --
-//                      the CA part of every document row of the request is a leading slice of it;
-//   rowinfo[h][g]   : what the attention kernel needs to build row (h, g)'s list itself:
-//                      {n, ca_n (-1: question row, dense range), ca_base, la_word, la_lo, t0, r, 0}.
-__device__ inline void prepass_head(const PlanView &pv, const uint32_t *__restrict__ la,
-                                    const uint32_t *__restrict__ ca, int32_t *__restrict__ ca_prefix,
-                                    int32_t *__restrict__ ca_list, int32_t *__restrict__ rowinfo, int h) {
-    const int tid = threadIdx.x;
-    const int ndocs = pv.num_docs, G = pv.num_tiles;
-    int32_t *pref = ca_prefix + static_cast<int64_t>(h) * ndocs;
-    int32_t *lst = ca_list + static_cast<int64_t>(h) * G;
-    __shared__ int sh[kCountThreads / 64];
-    head_ca_prefix(pv, ca, h, pref, lst, sh);  // the head's page list (G >= ndocs) as scratch
-    head_ca_list(pv, ca, h, pref, lst);
-    // per-row records
-    for (int g = tid; g < G; g += kCountThreads) {
-        int32_t *ri = rowinfo + (static_cast<int64_t>(h) * G + g) * 8;
-        const int d = pv.tile_doc[g];
-        if (d < 0) {
-            const int first = pv.req_first[-d - 1];
-            ri[0] = g - first + 1;
-            ri[1] = -1;
-            ri[2] = 0;
-            ri[3] = 0;
-            ri[4] = 0;
-            ri[5] = first;
-            ri[6] = 0;
-        } else {
-            const int r = pv.tile_local[g];
-            const int lo = r * (r + 1) / 2;
-            const int la_word = pv.doc_la_off[d] + h * pv.doc_la_w[d];
-            const int la_n = popcount_range(la + la_word, lo, lo + r);
-            ri[0] = pref[d] + la_n;
-            ri[1] = pref[d];
-            ri[2] = h * G + pv.req_first[pv.doc_req[d]];
-            ri[3] = la_word;
-            ri[4] = lo;
-            ri[5] = pv.doc_first[d];
-            ri[6] = r;
-        }
-        ri[7] = 0;
-    }
-}
-
 // V [N][Hkv][D] (bf16 or fp32, rounded to bf16) -> V^T tiles [Hkv][G][D][64] (each 64-token tile's
 // D rows of 128 bytes contiguous, so that the attention's tile loads cover one 16 KB block) with
 // the tokens of every 16-token group at vt_pos.  One workgroup of 256 threads per (64-token tile t,
 // kv head): the tile goes through LDS so that both the 2D-byte row reads and the 128-byte V^T row
 // writes are whole rows.
-template <int D, typename T>
+template <int D>
+constexpr int kTransposeLd = D + 2;  // padded LDS row (bf16 elements): column reads hit distinct banks
+
+template <int D, typename T, int NT>
 __device__ inline void transpose_tile(const T *__restrict__ v, uint16_t *__restrict__ vt, int Hkv, int64_t N, int t,
-                                      int kvh) {
-    constexpr int LD = D + 2;  // padded LDS row (bf16 elements): column reads hit distinct banks
+                                      int kvh, uint16_t *tile) {
+    constexpr int LD = kTransposeLd<D>;
     constexpr int CH = D / 8;  // 8-element chunks per token row
-    __shared__ uint16_t tile[64 * LD];
     const int tid = threadIdx.x;
     const int64_t tok0 = static_cast<int64_t>(t) * kTile;
     // read: 8 consecutive elements (16 or 32 bytes) of one token row per thread and pass
-    for (int x = tid; x < 64 * CH; x += 256) {
+    for (int x = tid; x < 64 * CH; x += NT) {
         const int r = x / CH, c = x % CH;
         const T *src = v + ((tok0 + r) * Hkv + kvh) * D + 8 * c;
         uint16_t *dst = tile + r * LD + 8 * c;
@@ -102,7 +59,7 @@ __device__ inline void transpose_tile(const T *__restrict__ v, uint16_t *__restr
     }
     __syncthreads();
     // V^T row d of this tile: 64 stored positions; thread writes 8 consecutive positions
-    for (int x = tid; x < D * 8; x += 256) {
+    for (int x = tid; x < D * 8; x += NT) {
         const int d = x / 8, c = x % 8;
         uint16_t w[8];
 #pragma unroll
@@ -116,6 +73,73 @@ __device__ inline void transpose_tile(const T *__restrict__ v, uint16_t *__restr
     }
 }
 
+// Tiles x0 .. x0 + n - 1 (n <= TPB) of the (kv head, tile) order x = kvh G + t, all staged in LDS at
+// once: every thread first loads its 16-byte chunks of all n tiles (one round trip to memory for
+// the workgroup), then the V^T rows are gathered from LDS and written.  NT threads.
+template <int D, typename T, int NT, int TPB>
+__device__ inline void transpose_tiles(const T *__restrict__ v, uint16_t *__restrict__ vt, int Hkv, int G, int x0,
+                                       int n, uint16_t *lds) {
+    constexpr int LD = kTransposeLd<D>;
+    constexpr int CH = D / 8;             // 8-element chunks per token row
+    constexpr int PER = 64 * CH;          // chunks per tile
+    constexpr int K = (TPB * PER + NT - 1) / NT;  // chunks per thread, at most
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const int tid = threadIdx.x;
+    u32x4 got[K];  // 8 bf16 each
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int x = tid + k * NT;
+        got[k] = u32x4{0u, 0u, 0u, 0u};
+        if (x < n * PER) {
+            const int j = x / PER, y = x % PER, r = y / CH, c = y % CH;
+            const int tile = x0 + j, t = tile % G, kvh = tile / G;
+            const T *src = v + ((static_cast<int64_t>(t) * kTile + r) * Hkv + kvh) * D + 8 * c;
+            if constexpr (sizeof(T) == 2) {
+                got[k] = *reinterpret_cast<const u32x4 *>(src);
+            } else {
+                const float4 a = *reinterpret_cast<const float4 *>(src);
+                const float4 b = *reinterpret_cast<const float4 *>(src + 4);
+                const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(f[2 * e])) |
+                           (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f[2 * e + 1]))) << 16);
+                got[k] = u32x4{w[0], w[1], w[2], w[3]};
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int x = tid + k * NT;
+        if (x < n * PER) {
+            const int j = x / PER, y = x % PER, r = y / CH, c = y % CH;
+            uint32_t *dst = reinterpret_cast<uint32_t *>(lds + (j * 64 + r) * LD + 8 * c);  // 4-byte aligned
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e] = got[k][e];
+        }
+    }
+    __syncthreads();
+    for (int x = tid; x < n * D * 8; x += NT) {
+        const int j = x / (D * 8), y = x % (D * 8), d = y / 8, c = y % 8;
+        const int tile = x0 + j, t = tile % G, kvh = tile / G;
+        const uint16_t *tl = lds + j * 64 * LD;
+        uint16_t w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = tl[static_cast<int>(vt_pos(8 * c + e)) * LD + d];
+        uint4 pk;
+        pk.x = w[0] | (uint32_t(w[1]) << 16);
+        pk.y = w[2] | (uint32_t(w[3]) << 16);
+        pk.z = w[4] | (uint32_t(w[5]) << 16);
+        pk.w = w[6] | (uint32_t(w[7]) << 16);
+        *reinterpret_cast<uint4 *>(vt + ((static_cast<int64_t>(kvh) * G + t) * D + d) * kTile + 8 * c) = pk;
+    }
+}
+
+// V^T tiles one workgroup of the decode-transpose launch stages together.
+template <int D>
+constexpr int kTransposeTpb = static_cast<int>(sizeof(DecodeOneLds) / (sizeof(uint16_t) * 64 * kTransposeLd<D>));
+
 // The attention kernel claims rows from the header's counters and raises flags in its status
 // word: both start at zero for every call.
 __device__ inline void clear_prefill_header(int *__restrict__ header) {
@@ -127,29 +151,32 @@ __device__ inline void clear_prefill_header(int *__restrict__ header) {
 template <int D, typename T>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const T *__restrict__ v, uint16_t *__restrict__ vt,
                                                           int Hkv, int64_t N, int *__restrict__ header) {
+    __shared__ uint16_t tile[64 * kTransposeLd<D>];
     if (blockIdx.x == 0 && blockIdx.y == 0) clear_prefill_header(header);
-    transpose_tile<D, T>(v, vt, Hkv, N, blockIdx.x, blockIdx.y);
+    transpose_tile<D, T, 256>(v, vt, Hkv, N, blockIdx.x, blockIdx.y, tile);
 }
 
-// Fused path: the bits pre-pass and the V^T transpose are independent, so they share one launch:
-// blocks 0 .. Hq-1 run the pre-pass of one q head each (short, latency-bound: they come first), the
-// other blocks transpose one (tile, kv head) each (bandwidth-bound) and the first of them clears
-// the header.  A plan of another layout skips the pre-pass (the attention kernel flags it).
+// Fused path, one launch: the single-launch decode of the layer's bits into the workspace CSR
+// (workgroups 0 .. ndec - 1, dispatched first: they are latency-bound) beside the V^T transpose,
+// one tile per workgroup, whose first workgroup clears the attention's row-queue counters (the
+// status word is the decode's).
 template <int D, typename T>
-__global__ __launch_bounds__(256) void fused_prep_kernel(PlanView pv, const uint32_t *__restrict__ la,
-                                                         const uint32_t *__restrict__ ca,
-                                                         int32_t *__restrict__ ca_prefix,
-                                                         int32_t *__restrict__ ca_list, int32_t *__restrict__ rowinfo,
-                                                         const T *__restrict__ v, uint16_t *__restrict__ vt, int Hq,
-                                                         int Hkv, int G, int *__restrict__ header) {
-    const int b = blockIdx.x;
-    if (b < Hq) {
-        if (plan_ok(pv)) prepass_head(pv, la, ca, ca_prefix, ca_list, rowinfo, b);
+__global__ __launch_bounds__(kOneThreads) void decode_transpose_kernel(
+    PlanView pv, const uint32_t *__restrict__ la, const uint32_t *__restrict__ ca, int la_words, int ca_words,
+    int32_t *__restrict__ row_ptr, int32_t *__restrict__ col_idx, int32_t *__restrict__ status, int splits,
+    int question_nnz, const T *__restrict__ v, uint16_t *__restrict__ vt, int Hkv, int G, int *__restrict__ header) {
+    __shared__ DecodeOneLds lds;  // a transpose workgroup stages its kTransposeTpb<D> tiles here
+    constexpr int TPB = kTransposeTpb<D>;
+    static_assert(TPB >= 1, "a tile fits");
+    const int b = blockIdx.x, ndec = pv.num_q_heads * splits;
+    if (b < ndec) {
+        decode_one_block(pv, la, ca, la_words, ca_words, row_ptr, col_idx, status, splits, question_nnz, lds, b);
         return;
     }
-    const int x = b - Hq;
-    if (x == 0) clear_prefill_header(header);
-    transpose_tile<D, T>(v, vt, Hkv, static_cast<int64_t>(G) * kTile, x % G, x / G);
+    const int x0 = (b - ndec) * TPB;
+    if (x0 == 0 && threadIdx.x < kPrefillQueues) header[threadIdx.x] = 0;
+    transpose_tiles<D, T, kOneThreads, TPB>(v, vt, Hkv, G, x0, min(TPB, G * Hkv - x0),
+                                            reinterpret_cast<uint16_t *>(&lds));
 }
 
 __global__ void cast_bf16_kernel(const float *__restrict__ src, __bf16 *__restrict__ dst, int64_t n) {
@@ -183,22 +210,30 @@ hipError_t launch_transpose_v(const HostLayout &hl, const void *v, bool fp32, ui
     return hipGetLastError();
 }
 
-hipError_t launch_fused_prep(const HostLayout &hl, const PlanView &pv, const uint32_t *la, const uint32_t *ca,
-                             int32_t *ca_prefix, int32_t *ca_list, int32_t *rowinfo, const void *v, bool fp32,
-                             uint16_t *vt, int *header, hipStream_t stream) {
-    if (hl.G == 0) return hipSuccess;
-    const unsigned grid = static_cast<unsigned>(hl.Hq + int64_t(hl.G) * hl.Hkv);
-#define SIFT_FUSED_PREP(DD, TT)                                                                                  \
-    fused_prep_kernel<DD, TT><<<grid, 256, 0, stream>>>(pv, la, ca, ca_prefix, ca_list, rowinfo,               \
-                                                        static_cast<const TT *>(v), vt, hl.Hq, hl.Hkv, hl.G, header)
+bool decode_transpose_fits(const HostLayout &hl) { return decode_one_fits(hl); }
+
+hipError_t launch_decode_transpose(const HostLayout &hl, const PlanView &pv, const uint32_t *la, const uint32_t *ca,
+                                   int32_t *row_ptr, int32_t *col_idx, int32_t *status, const void *v, bool fp32,
+                                   uint16_t *vt, int *header, hipStream_t stream) {
+    if (!decode_one_fits(hl)) return hipErrorInvalidValue;
+    const int splits = decode_one_splits(hl);
+    const int64_t tiles = int64_t(hl.G) * hl.Hkv, tpb = hl.D == 128 ? kTransposeTpb<128> : kTransposeTpb<64>;
+    const unsigned grid = static_cast<unsigned>(int64_t(hl.Hq) * splits + (tiles + tpb - 1) / tpb);
+    const int qn = static_cast<int>(hl.question_nnz);
+    const int law = static_cast<int>(hl.la_words), caw = static_cast<int>(hl.ca_words);
+#define SIFT_DT(DD, TT)                                                                                 \
+    decode_transpose_kernel<DD, TT><<<grid, kOneThreads, 0, stream>>>(pv, la, ca, law, caw, row_ptr, col_idx, \
+                                                                      status, splits, qn,                \
+                                                                      static_cast<const TT *>(v), vt,    \
+                                                                      hl.Hkv, hl.G, header)
     if (hl.D == 128) {
-        if (fp32) SIFT_FUSED_PREP(128, float);
-        else SIFT_FUSED_PREP(128, __bf16);
+        if (fp32) SIFT_DT(128, float);
+        else SIFT_DT(128, __bf16);
     } else {
-        if (fp32) SIFT_FUSED_PREP(64, float);
-        else SIFT_FUSED_PREP(64, __bf16);
+        if (fp32) SIFT_DT(64, float);
+        else SIFT_DT(64, __bf16);
     }
-#undef SIFT_FUSED_PREP
+#undef SIFT_DT
     return hipGetLastError();
 }
 

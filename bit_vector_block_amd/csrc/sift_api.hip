@@ -218,19 +218,19 @@ size_t decode_workspace_bytes(const HostLayout &hl) {
 }
 
 // Prefill workspace: the header (row-queue counters, status word), V^T (bf16 tiles
-// [Hkv][G][D][64]); for SIFT_FP32 inputs the bf16 copies of Q and K follow.  The fused path (no
-// CSR) appends its pre-pass tables: ca_prefix [Hq][ndocs], ca_list [Hq][G], rowinfo [Hq][G][8]
-// (int32).
+// [Hkv][G][D][64]); for SIFT_FP32 inputs the bf16 copies of Q and K follow.
 static size_t prefill_workspace_bytes(const HostLayout &hl, sift_dtype dtype) {
     const size_t N = size_t(hl.G) * kTile;
     const size_t vt = kWorkspaceHeader + align256(2 * N * hl.Hkv * hl.D);
     if (dtype != SIFT_FP32) return vt;
     return vt + align256(2 * N * hl.Hq * hl.D) + align256(2 * N * hl.Hkv * hl.D);
 }
-static size_t bits_tables_bytes(const HostLayout &hl) {
-    const size_t rows = size_t(hl.Hq) * size_t(hl.G > 0 ? hl.G : 1);
-    return align256(4 * size_t(hl.Hq) * size_t(hl.ndocs > 0 ? hl.ndocs : 1)) + align256(4 * rows) +
-           align256(32 * rows);
+// The fused path's tables past the prefill workspace: the CSR its decode writes (row_ptr [Hq G + 1],
+// col_idx [max_nnz]) and, for layouts beyond the single-launch decode, that decode's scratch.
+static size_t fused_tables_bytes(const HostLayout &hl) {
+    const size_t csr = align256(4 * (size_t(hl.Hq) * size_t(hl.G) + 1)) +
+                       align256(4 * size_t(hl.max_nnz > 0 ? hl.max_nnz : 1));
+    return csr + (decode_transpose_fits(hl) ? 0 : decode_workspace_bytes(hl) - kWorkspaceHeader);
 }
 
 // Scratch of the allocation-free decode (sift_decode_bits_noalloc): one array per GPU, in the
@@ -324,7 +324,7 @@ size_t sift_workspace_bytes(const sift_layout *layout, sift_dtype dtype) {
     HostLayout hl;
     if (build_layout(layout, &hl) != SIFT_OK) return 0;
     if (dtype != SIFT_BF16 && dtype != SIFT_FP32) return 0;
-    return std::max(decode_workspace_bytes(hl), prefill_workspace_bytes(hl, dtype) + bits_tables_bytes(hl));
+    return std::max(decode_workspace_bytes(hl), prefill_workspace_bytes(hl, dtype) + fused_tables_bytes(hl));
 }
 
 sift_status sift_plan_upload(const sift_layout *layout, void *d_plan, size_t plan_bytes,
@@ -424,8 +424,8 @@ sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan, c
         k = kb;
     }
     if (launch_transpose_v(hl, d_v, dtype == SIFT_FP32, vt, header, stream) != hipSuccess ||
-        launch_prefill(hl, pv, q, k, vt, d_row_ptr, d_col_idx, col_entries, nullptr, nullptr, nullptr, scale,
-                       d_out, d_lse, header, stream) != hipSuccess)
+        launch_prefill(hl, pv, q, k, vt, d_row_ptr, d_col_idx, col_entries, scale, d_out, d_lse, header,
+                       stream) != hipSuccess)
         return SIFT_ERR_HIP;
     return SIFT_OK;
 }
@@ -445,12 +445,10 @@ sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_pl
     if (!aligned16(d_q) || !aligned16(d_k) || !aligned16(d_v) || !aligned16(d_out) ||
         (d_workspace && !aligned16(d_workspace)))
         return SIFT_ERR_INVALID;
-    // a row's LA bits are read as at most 64 words: documents of at most 1984 tiles
-    if (hl.max_doc_tiles > 1984) return SIFT_ERR_UNSUPPORTED;
     if (!(scale > 0.0f)) scale = 1.0f / sqrtf(float(hl.D));
     if (!isfinite(scale)) return SIFT_ERR_INVALID;
     const size_t base = prefill_workspace_bytes(hl, dtype);
-    const size_t need = base + bits_tables_bytes(hl);
+    const size_t need = base + fused_tables_bytes(hl);
     if (!d_workspace || workspace_bytes < need) return SIFT_ERR_CAPACITY;
     const PlanView pv = plan_view(hl, d_plan);
     const uint16_t *q = static_cast<const uint16_t *>(d_q);
@@ -470,15 +468,22 @@ sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_pl
         q = qb;
         k = kb;
     }
-    const size_t rows = size_t(hl.Hq) * size_t(hl.G);
     char *tb = ws + base;
-    int32_t *ca_prefix = reinterpret_cast<int32_t *>(tb);
-    int32_t *ca_list = reinterpret_cast<int32_t *>(tb + align256(4 * size_t(hl.Hq) * size_t(hl.ndocs > 0 ? hl.ndocs : 1)));
-    int32_t *rowinfo = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ca_list) + align256(4 * rows));
-    if (launch_fused_prep(hl, pv, d_la, d_ca, ca_prefix, ca_list, rowinfo, d_v, dtype == SIFT_FP32, vt, header,
-                          stream) != hipSuccess ||
-        launch_prefill(hl, pv, q, k, vt, nullptr, nullptr, 0, rowinfo, ca_list, d_la, scale, d_out, d_lse,
-                       header, stream) != hipSuccess)
+    int32_t *row_ptr = reinterpret_cast<int32_t *>(tb);
+    int32_t *col_idx = reinterpret_cast<int32_t *>(tb + align256(4 * (size_t(hl.Hq) * size_t(hl.G) + 1)));
+    int32_t *status = header + kStatusWord;
+    if (decode_transpose_fits(hl)) {
+        if (launch_decode_transpose(hl, pv, d_la, d_ca, row_ptr, col_idx, status, d_v, dtype == SIFT_FP32, vt,
+                                    header, stream) != hipSuccess)
+            return SIFT_ERR_HIP;
+    } else {  // the transpose clears the header, then the decode sets the status word
+        void *scratch = reinterpret_cast<char *>(col_idx) + align256(4 * size_t(hl.max_nnz > 0 ? hl.max_nnz : 1));
+        if (launch_transpose_v(hl, d_v, dtype == SIFT_FP32, vt, header, stream) != hipSuccess ||
+            launch_decode(hl, pv, d_la, d_ca, row_ptr, col_idx, scratch, status, stream) != hipSuccess)
+            return SIFT_ERR_HIP;
+    }
+    if (launch_prefill(hl, pv, q, k, vt, row_ptr, col_idx, hl.max_nnz, scale, d_out, d_lse, header, stream) !=
+        hipSuccess)
         return SIFT_ERR_HIP;
     return SIFT_OK;
 }

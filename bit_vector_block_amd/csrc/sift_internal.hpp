@@ -103,11 +103,13 @@ size_t decode_workspace_bytes(const HostLayout &hl);
 hipError_t launch_decode(const HostLayout &hl, const PlanView &pv, const uint32_t *la,
                          const uint32_t *ca, int32_t *row_ptr, int32_t *col_idx, void *scratch,
                          int32_t *status, hipStream_t stream);
-// Fused path (no CSR), one launch: per head, the request-level CA page lists and per-row list
-// records; and the V^T transpose with the header cleared, as launch_transpose_v.
-hipError_t launch_fused_prep(const HostLayout &hl, const PlanView &pv, const uint32_t *la, const uint32_t *ca,
-                             int32_t *ca_prefix, int32_t *ca_list, int32_t *rowinfo, const void *v, bool fp32,
-                             uint16_t *vt, int *header, hipStream_t stream);
+// Fused path: the single-launch decode into a CSR of the workspace beside the V^T transpose, in
+// one launch, for layouts that decode_transpose_fits (the others run launch_transpose_v, then
+// launch_decode).  The decode writes the status word; the transpose clears the row-queue counters.
+bool decode_transpose_fits(const HostLayout &hl);
+hipError_t launch_decode_transpose(const HostLayout &hl, const PlanView &pv, const uint32_t *la, const uint32_t *ca,
+                                   int32_t *row_ptr, int32_t *col_idx, int32_t *status, const void *v, bool fp32,
+                                   uint16_t *vt, int *header, hipStream_t stream);
 // Offline encoder (tile masses of dense attention, then top-p selection into LA/CA words).
 // `status` (may be null): the caller's device word for the sift_device_flag bits.
 // The tile-mass kernel is persistent: each workgroup claims work items from its XCD's queue
@@ -128,13 +130,11 @@ hipError_t launch_cast_bf16(const float *src, uint16_t *dst, int64_t n, hipStrea
 // from, and the status word); `header` is the workspace start.
 hipError_t launch_transpose_v(const HostLayout &hl, const void *v, bool fp32, uint16_t *vt, int *header,
                               hipStream_t stream);
-// Attention over the CSR (rowinfo == nullptr; col_entries readable col_idx entries) or, fused,
-// over lists the kernel builds from the pre-pass records, the CA page lists and the LA bits
-// (row_ptr, col_idx unused).  `header`: the workspace start (counters, status word).
+// Attention over the CSR (col_entries readable col_idx entries).  `header`: the workspace start
+// (row-queue counters, status word).
 hipError_t launch_prefill(const HostLayout &hl, const PlanView &pv, const uint16_t *q,
                           const uint16_t *k, const uint16_t *vt, const int32_t *row_ptr,
-                          const int32_t *col_idx, int64_t col_entries, const int32_t *rowinfo,
-                          const int32_t *ca_list, const uint32_t *la_bits, float scale, float *out, float *lse,
+                          const int32_t *col_idx, int64_t col_entries, float scale, float *out, float *lse,
                           int *header, hipStream_t stream);
 
 }  // namespace sift

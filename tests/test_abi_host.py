@@ -177,11 +177,11 @@ def test_prefill_bits_validation():
     st = lib.sift_sparse_prefill_bits(lay.ref, a, a, a, a, a, a, B.SIFT_BF16, ctypes.c_float(0.0),
                                       a, vp(0), a, 16, vp(0))
     assert st == B.SIFT_ERR_CAPACITY
-    # a document of more than 1984 tiles
-    big = sift.Layout([1], [1985 * 64], [0], 1, 1, 64)
-    st = lib.sift_sparse_prefill_bits(big.ref, a, a, a, a, a, a, B.SIFT_BF16, ctypes.c_float(0.0),
-                                      a, vp(0), a, 1 << 40, vp(0))
-    assert st == B.SIFT_ERR_UNSUPPORTED
+    # the fused call's workspace holds the CSR its decode writes (max_nnz entries) on top of the
+    # prefill's V^T; layouts past the single-launch decode also hold that decode's scratch
+    for lay2 in (lay, sift.Layout([1], [1985 * 64], [0], 1, 1, 64)):
+        fused = lib.sift_workspace_bytes(lay2.ref, B.SIFT_BF16)
+        assert fused >= 256 + 2 * lay2.padded_tokens * 1 * 64 + 4 * (lay2.num_rows + 1) + 4 * lay2.csr_max_nnz
 
 
 def test_encoder_validation():

@@ -101,18 +101,19 @@ def test_decode_empty_layout():
     assert rp.tolist() == [0] and ci.size == 0
 
 
-# Layouts at and past the single-launch decode's per-head LDS bounds (2048 rows, 1024 documents,
-# 64 tiles per document); past them the decode runs as two launches.
-@pytest.mark.parametrize("name,req_num_docs,doc_tiles,question_len", [
-    ("at_bounds", [1024], [2] * 1024, [0]),               # G 2048, 1024 documents
-    ("rows_past_bound", [33], [64] * 33, [70]),           # G 2114
-    ("docs_past_bound", [515, 515], [1] * 1030, [64, 1]),  # 1030 documents
-    ("doc_tiles_past_bound", [2], [65, 3], [10]),         # a 65-tile document
+# Layouts at and past the single-launch decode's bounds (2048 rows per head, 512 documents of at
+# most 64 tiles, 8192 LA and 2048 CA words in the batch); past them the decode runs as two launches.
+@pytest.mark.parametrize("name,req_num_docs,doc_tiles,question_len,hq", [
+    ("at_bounds", [512], [4] * 512, [0], 1),                # G 2048, 512 documents
+    ("rows_past_bound", [33], [64] * 33, [70], 1),          # G 2114
+    ("docs_past_bound", [260, 260], [1] * 520, [64, 1], 1),  # 520 documents
+    ("doc_tiles_past_bound", [2], [65, 3], [10], 1),        # a 65-tile document
+    ("words_past_bound", [16], [64] * 16, [64], 8),         # 8320 LA words
 ])
-def test_decode_single_launch_bounds(name, req_num_docs, doc_tiles, question_len):
+def test_decode_single_launch_bounds(name, req_num_docs, doc_tiles, question_len, hq):
     doc_len = [64 * t - (i % 7) for i, t in enumerate(doc_tiles)]
     r = len(req_num_docs)
-    case = W.make_case(name, 11, req_num_docs, doc_len, question_len, 1, 1, 64,
-                       np.full((r, 1), 0.3), np.full((r, 1), 0.2))
-    print(f"decode {name}: G={case.q.shape[0] // 64} docs={len(doc_len)}", flush=True)
+    case = W.make_case(name, 11, req_num_docs, doc_len, question_len, hq, 1, 64,
+                       np.full((r, hq), 0.3), np.full((r, hq), 0.2))
+    print(f"decode {name}: G={case.q.shape[0] // 64} docs={len(doc_len)} la={case.la_words.size}", flush=True)
     _check(case)

@@ -72,10 +72,10 @@ def test_fused_long_documents_multiword_rows():
     assert_close(out[toks, heads], ref, "long docs")
 
 
-def test_fused_at_the_document_size_limit():
-    """A document of 1,984 tiles, the largest the fused pre-pass lists (one more is rejected on the
-    host): the fused call equals the CSR path, and sampled rows match the oracle."""
-    case = W.make_case("doc-limit", 1984, [1], [1984 * 64], [64], 2, 1, 64,
+def test_fused_long_document():
+    """A document of 2,000 tiles (its decode takes the two-launch path): the fused call equals the
+    CSR path, and sampled rows match the oracle."""
+    case = W.make_case("doc-limit", 1984, [1], [2000 * 64], [64], 2, 1, 64,
                        np.full((1, 2), 0.02), np.full((1, 2), 0.02))
     out, _ = _same_as_csr_path(case)
     rng = np.random.default_rng(5)
@@ -83,7 +83,7 @@ def test_fused_at_the_document_size_limit():
     toks = np.concatenate([rng.choice(valid, 200), valid[-128:]]).astype(np.int64)
     heads = rng.integers(0, case.num_q_heads, size=toks.size).astype(np.int32)
     ref, _ = oracle.attention(case, heads=heads, tokens=toks)
-    assert_close(out[toks, heads], ref, "document at the size limit")
+    assert_close(out[toks, heads], ref, "long document")
 
 
 def test_fused_empty_and_dense_bits():
