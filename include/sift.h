@@ -211,18 +211,22 @@ sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan,
                                 void *d_workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * sift_sparse_prefill_bits: the same attention, with the decode fused into it (no CSR).  The
- * SIFT technical summary's "Design del Sistema" has the attention kernel read the bit vectors
- * themselves; here a small pre-pass lists each request's CA-marked pages once per head (the
- * CA part of every row of a document is a leading slice of that list), and each attention
- * workgroup builds its rows' tile lists from that slice and from the row's own LA bits.
+ * sift_sparse_prefill_bits: the same attention, with the decode folded into the call: the caller
+ * passes the bits and gets the attention output, no CSR.  The SIFT technical summary's "Design
+ * del Sistema" has the attention read the bit vectors; here one launch decodes them into a CSR
+ * in the workspace (each workgroup counts its q head's rows in closed form and lists its share of
+ * them) while its other workgroups write V^T, and the attention kernel then reads that CSR.
+ * Layouts past the single-launch decode's bounds (more than 2048 tiles, 512 documents or 64 tiles
+ * in a document, or more than 8192 LA words) run the V^T transpose and the two-launch decode
+ * first instead.
  * d_la, d_ca: the layer's bits as for sift_decode_bits.  Other arguments, the output and the
  * 16-byte alignment rule as for sift_sparse_prefill; the result is bit-identical to
  * sift_decode_bits followed by sift_sparse_prefill on the same bits.
- * d_workspace: >= sift_workspace_bytes(layout, dtype) bytes; status word as for
+ * d_workspace: >= sift_workspace_bytes(layout, dtype) bytes (it also holds the CSR: 4 (Hq G + 1)
+ * + 4 sift_csr_max_nnz() bytes more than sift_sparse_prefill needs); status word as for
  * sift_sparse_prefill.
  * Errors: SIFT_ERR_INVALID, SIFT_ERR_CAPACITY (workspace), SIFT_ERR_UNSUPPORTED (head_dim, tile,
- * a document of more than 1984 tiles), SIFT_ERR_HIP.
+ * nnz bound >= 2^31), SIFT_ERR_HIP.
  */
 sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_plan,
                                      const uint32_t *d_la, const uint32_t *d_ca,
