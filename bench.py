@@ -71,8 +71,11 @@ def profiled_traffic(workload):
     for line in lines:
         if line.startswith("traffic-json:"):
             info = json.loads(line.split(":", 1)[1])
-            try:
-                src = open(os.path.join(ROOT, info["kernel_source"]), "rb").read()
+            sources = info["kernel_source"]
+            if isinstance(sources, str):
+                sources = [sources]
+            try:  # the listed sources, concatenated in order
+                src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in sources)
             except OSError:
                 return None
             if info.get("workload") == workload and \
