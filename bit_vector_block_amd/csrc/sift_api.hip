@@ -430,6 +430,84 @@ sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan, c
     return SIFT_OK;
 }
 
+// The fused path in two steps.  prepare: fp32 inputs cast, the bits decoded into the workspace
+// CSR and V^T written (one launch where the layout allows, see launch_decode_transpose); attend:
+// the attention kernel over them.  Both take a validated call.
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static sift_status check_bits_call(const HostLayout &hl, sift_dtype dtype, const void *d_plan, size_t workspace_bytes,
+                                   const void *d_workspace) {
+    if (dtype != SIFT_BF16 && dtype != SIFT_FP32) return SIFT_ERR_INVALID;
+    if (hl.G == 0) return SIFT_OK;
+    if (!d_plan || (d_workspace && !aligned16(d_workspace))) return SIFT_ERR_INVALID;
+    if (!d_workspace || workspace_bytes < prefill_workspace_bytes(hl, dtype) + fused_tables_bytes(hl))
+        return SIFT_ERR_CAPACITY;
+    return SIFT_OK;
+}
+
+struct BitsWorkspace {
+    int *header;
+    uint16_t *vt, *qb, *kb;  // V^T; the bf16 copies of fp32 Q and K
+    int32_t *row_ptr, *col_idx;
+    void *decode_scratch;    // the two-launch decode's scratch (layouts past the single launch)
+};
+static BitsWorkspace bits_workspace(const HostLayout &hl, sift_dtype dtype, void *d_workspace) {
+    const int64_t N = int64_t(hl.G) * kTile;
+    const int64_t nq = N * hl.Hq * hl.D, nkv = N * hl.Hkv * hl.D;
+    char *ws = static_cast<char *>(d_workspace);
+    BitsWorkspace w;
+    w.header = reinterpret_cast<int *>(ws);
+    w.vt = reinterpret_cast<uint16_t *>(ws + kWorkspaceHeader);
+    char *ws2 = ws + kWorkspaceHeader + align256(2 * size_t(nkv));
+    w.qb = reinterpret_cast<uint16_t *>(ws2);
+    w.kb = reinterpret_cast<uint16_t *>(ws2 + align256(2 * size_t(nq)));
+    char *tb = ws + prefill_workspace_bytes(hl, dtype);
+    w.row_ptr = reinterpret_cast<int32_t *>(tb);
+    w.col_idx = reinterpret_cast<int32_t *>(tb + align256(4 * (size_t(hl.Hq) * size_t(hl.G) + 1)));
+    w.decode_scratch = reinterpret_cast<char *>(w.col_idx) + align256(4 * size_t(hl.max_nnz > 0 ? hl.max_nnz : 1));
+    return w;
+}
+
+static sift_status prepare_bits(const HostLayout &hl, const PlanView &pv, const uint32_t *d_la, const uint32_t *d_ca,
+                                const void *d_q, const void *d_k, const void *d_v, sift_dtype dtype,
+                                void *d_workspace, hipStream_t stream) {
+    const BitsWorkspace w = bits_workspace(hl, dtype, d_workspace);
+    const int64_t N = int64_t(hl.G) * kTile;
+    if (dtype == SIFT_FP32 &&
+        (launch_cast_bf16(static_cast<const float *>(d_q), w.qb, N * hl.Hq * hl.D, stream) != hipSuccess ||
+         launch_cast_bf16(static_cast<const float *>(d_k), w.kb, N * hl.Hkv * hl.D, stream) != hipSuccess))
+        return SIFT_ERR_HIP;
+    int32_t *status = w.header + kStatusWord;
+    if (decode_transpose_fits(hl)) {
+        if (launch_decode_transpose(hl, pv, d_la, d_ca, w.row_ptr, w.col_idx, status, d_v, dtype == SIFT_FP32, w.vt,
+                                    w.header, stream) != hipSuccess)
+            return SIFT_ERR_HIP;
+    } else {  // the transpose clears the header, then the decode sets the status word
+        if (launch_transpose_v(hl, d_v, dtype == SIFT_FP32, w.vt, w.header, stream) != hipSuccess ||
+            launch_decode(hl, pv, d_la, d_ca, w.row_ptr, w.col_idx, w.decode_scratch, status, stream) != hipSuccess)
+            return SIFT_ERR_HIP;
+    }
+    return SIFT_OK;
+}
+
+static sift_status attend_prepared(const HostLayout &hl, const PlanView &pv, const void *d_q, const void *d_k,
+                                   sift_dtype dtype, float scale, float *d_out, float *d_lse, void *d_workspace,
+                                   hipStream_t stream) {
+    const BitsWorkspace w = bits_workspace(hl, dtype, d_workspace);
+    const uint16_t *q = dtype == SIFT_FP32 ? w.qb : static_cast<const uint16_t *>(d_q);
+    const uint16_t *k = dtype == SIFT_FP32 ? w.kb : static_cast<const uint16_t *>(d_k);
+    if (launch_prefill(hl, pv, q, k, w.vt, w.row_ptr, w.col_idx, hl.max_nnz, scale, d_out, d_lse, w.header, stream) !=
+        hipSuccess)
+        return SIFT_ERR_HIP;
+    return SIFT_OK;
+}
+
+// scale <= 0 (or NaN) takes 1 / sqrt(D); a non-finite result is invalid
+static bool resolve_scale(const HostLayout &hl, float &scale) {
+    if (!(scale > 0.0f)) scale = 1.0f / sqrtf(float(hl.D));
+    return isfinite(scale);
+}
+
 sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_plan, const uint32_t *d_la,
                                      const uint32_t *d_ca, const void *d_q, const void *d_k, const void *d_v,
                                      sift_dtype dtype, float scale, float *d_out, float *d_lse,
@@ -439,53 +517,14 @@ sift_status sift_sparse_prefill_bits(const sift_layout *layout, const void *d_pl
     if (st != SIFT_OK) return st;
     if (dtype != SIFT_BF16 && dtype != SIFT_FP32) return SIFT_ERR_INVALID;
     if (hl.G == 0) return SIFT_OK;
-    if (!d_plan || !d_q || !d_k || !d_v || !d_out) return SIFT_ERR_INVALID;
+    if (!d_q || !d_k || !d_v || !d_out) return SIFT_ERR_INVALID;
     if ((hl.la_words > 0 && !d_la) || (hl.ca_words > 0 && !d_ca)) return SIFT_ERR_INVALID;
-    auto aligned16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-    if (!aligned16(d_q) || !aligned16(d_k) || !aligned16(d_v) || !aligned16(d_out) ||
-        (d_workspace && !aligned16(d_workspace)))
-        return SIFT_ERR_INVALID;
-    if (!(scale > 0.0f)) scale = 1.0f / sqrtf(float(hl.D));
-    if (!isfinite(scale)) return SIFT_ERR_INVALID;
-    const size_t base = prefill_workspace_bytes(hl, dtype);
-    const size_t need = base + fused_tables_bytes(hl);
-    if (!d_workspace || workspace_bytes < need) return SIFT_ERR_CAPACITY;
+    if (!aligned16(d_q) || !aligned16(d_k) || !aligned16(d_v) || !aligned16(d_out)) return SIFT_ERR_INVALID;
+    if (!resolve_scale(hl, scale)) return SIFT_ERR_INVALID;
+    if ((st = check_bits_call(hl, dtype, d_plan, workspace_bytes, d_workspace)) != SIFT_OK) return st;
     const PlanView pv = plan_view(hl, d_plan);
-    const uint16_t *q = static_cast<const uint16_t *>(d_q);
-    const uint16_t *k = static_cast<const uint16_t *>(d_k);
-    const int64_t N = int64_t(hl.G) * kTile;
-    const int64_t nq = N * hl.Hq * hl.D, nkv = N * hl.Hkv * hl.D;
-    char *ws = static_cast<char *>(d_workspace);
-    int *header = reinterpret_cast<int *>(ws);
-    uint16_t *vt = reinterpret_cast<uint16_t *>(ws + kWorkspaceHeader);
-    if (dtype == SIFT_FP32) {
-        char *ws2 = ws + kWorkspaceHeader + align256(2 * size_t(nkv));
-        uint16_t *qb = reinterpret_cast<uint16_t *>(ws2);
-        uint16_t *kb = reinterpret_cast<uint16_t *>(ws2 + align256(2 * size_t(nq)));
-        if (launch_cast_bf16(static_cast<const float *>(d_q), qb, nq, stream) != hipSuccess ||
-            launch_cast_bf16(static_cast<const float *>(d_k), kb, nkv, stream) != hipSuccess)
-            return SIFT_ERR_HIP;
-        q = qb;
-        k = kb;
-    }
-    char *tb = ws + base;
-    int32_t *row_ptr = reinterpret_cast<int32_t *>(tb);
-    int32_t *col_idx = reinterpret_cast<int32_t *>(tb + align256(4 * (size_t(hl.Hq) * size_t(hl.G) + 1)));
-    int32_t *status = header + kStatusWord;
-    if (decode_transpose_fits(hl)) {
-        if (launch_decode_transpose(hl, pv, d_la, d_ca, row_ptr, col_idx, status, d_v, dtype == SIFT_FP32, vt,
-                                    header, stream) != hipSuccess)
-            return SIFT_ERR_HIP;
-    } else {  // the transpose clears the header, then the decode sets the status word
-        void *scratch = reinterpret_cast<char *>(col_idx) + align256(4 * size_t(hl.max_nnz > 0 ? hl.max_nnz : 1));
-        if (launch_transpose_v(hl, d_v, dtype == SIFT_FP32, vt, header, stream) != hipSuccess ||
-            launch_decode(hl, pv, d_la, d_ca, row_ptr, col_idx, scratch, status, stream) != hipSuccess)
-            return SIFT_ERR_HIP;
-    }
-    if (launch_prefill(hl, pv, q, k, vt, row_ptr, col_idx, hl.max_nnz, scale, d_out, d_lse, header, stream) !=
-        hipSuccess)
-        return SIFT_ERR_HIP;
-    return SIFT_OK;
+    if ((st = prepare_bits(hl, pv, d_la, d_ca, d_q, d_k, d_v, dtype, d_workspace, stream)) != SIFT_OK) return st;
+    return attend_prepared(hl, pv, d_q, d_k, dtype, scale, d_out, d_lse, d_workspace, stream);
 }
 
 size_t sift_encode_masses_bytes(const sift_layout *layout) {

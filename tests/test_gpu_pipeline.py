@@ -1,5 +1,5 @@
-"""GPU: the multi-layer pipeline (per-layer bits from pinned host memory, copied one layer ahead
-on a side stream) gives, layer by layer, exactly the single-layer result, which matches the oracle."""
+"""GPU: the multi-layer pipeline (per-layer bits from pinned host memory, copied ahead on a side
+stream) gives, layer by layer, exactly the single-layer result, which matches the oracle."""
 import numpy as np
 import pytest
 import torch
