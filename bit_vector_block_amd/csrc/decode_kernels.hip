@@ -192,7 +192,7 @@ hipError_t launch_decode(const HostLayout &hl, const PlanView &pv, const uint32_
         return hipGetLastError();
     }
     if (decode_one_fits(hl)) {
-        const int splits = decode_one_splits(hl);
+        const int splits = decode_one_splits(hl, kDecodeOneTarget);
         decode_one_kernel<<<static_cast<unsigned>(hl.Hq * splits), kOneThreads, 0, stream>>>(
             pv, la, ca, static_cast<int>(hl.la_words), static_cast<int>(hl.ca_words), row_ptr, col_idx, status,
             splits, static_cast<int>(hl.question_nnz));

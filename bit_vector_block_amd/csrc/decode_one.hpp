@@ -61,12 +61,17 @@ inline bool decode_one_fits(const HostLayout &hl) {
            hl.ca_words <= int64_t(kOneCaK) * kOneThreads;
 }
 
-// Workgroups of the single launch: about 256 in all; each fills at most 1024 rows of its head (64
-// per wavefront) and, where the head has enough, at least 16.
-inline int decode_one_splits(const HostLayout &hl) {
+// Workgroups per q head of the single launch, for about `target` workgroups in all; each fills at
+// most 1024 rows of its head (64 per wavefront) and, where the head has enough, at least 16.
+inline int decode_one_splits(const HostLayout &hl, int target) {
     const int64_t most = std::max<int64_t>(1, (hl.G + 15) / 16), least = (hl.G + 1023) / 1024;
-    return static_cast<int>(std::max<int64_t>(least, std::min<int64_t>(most, (256 + hl.Hq - 1) / hl.Hq)));
+    return static_cast<int>(std::max<int64_t>(least, std::min<int64_t>(most, (target + hl.Hq - 1) / hl.Hq)));
 }
+// Alone, the decode is fastest spread over about 256 workgroups; beside the V^T transpose in the
+// fused path's launch, over about 64, which leaves more of the chip to the transpose (config 2:
+// 345.8 against 349.6 us per fused call, one process).
+constexpr int kDecodeOneTarget = 256;
+constexpr int kDecodeTransposeTarget = 64;
 
 // Workgroup `bid` (of Hq * splits, kOneThreads threads) of the single-launch decode; L: its LDS.
 // After the plan check, all of its loads go out in one round: the plan records it needs and every

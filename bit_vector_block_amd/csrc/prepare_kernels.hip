@@ -216,7 +216,7 @@ hipError_t launch_decode_transpose(const HostLayout &hl, const PlanView &pv, con
                                    int32_t *row_ptr, int32_t *col_idx, int32_t *status, const void *v, bool fp32,
                                    uint16_t *vt, int *header, hipStream_t stream) {
     if (!decode_one_fits(hl)) return hipErrorInvalidValue;
-    const int splits = decode_one_splits(hl);
+    const int splits = decode_one_splits(hl, kDecodeTransposeTarget);
     const int64_t tiles = int64_t(hl.G) * hl.Hkv, tpb = hl.D == 128 ? kTransposeTpb<128> : kTransposeTpb<64>;
     const unsigned grid = static_cast<unsigned>(int64_t(hl.Hq) * splits + (tiles + tpb - 1) / tpb);
     const int qn = static_cast<int>(hl.question_nnz);
