@@ -247,11 +247,11 @@ __device__ __forceinline__ bool needs_mask(int t, int kv_valid, const RowCtx &c)
 __device__ __forceinline__ void apply_mask(f32x16 &s, int t, int kv_valid, const RowCtx &c) {
     const int hi = c.lane >> 5, kh = c.wave >> 1;
     const int lim = min(kv_valid, c.qi - (t - c.g) * kTile + 1);  // keys < lim survive
+    // key of register i = 32 kh + 4 hi + (8 (i / 4) + i % 4): compare the constant part with the
+    // limit less the lane's part
+    const int lk = lim - 32 * kh - 4 * hi;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int key = 32 * kh + 8 * (i >> 2) + 4 * hi + (i & 3);
-        s[i] = key < lim ? s[i] : -INFINITY;
-    }
+    for (int i = 0; i < 16; ++i) s[i] = 8 * (i >> 2) + (i & 3) < lk ? s[i] : -INFINITY;
 }
 
 // Raise the reference max when a score of the tile exceeds it by more than kLazyLog2 (decided
@@ -271,6 +271,16 @@ __device__ __forceinline__ void lazy_raise(WaveState<D> &st, float lmax, float &
         for (int db = 0; db < D / 32; ++db) st.acc_o[db] *= alpha;
         nbias = (m_new == -INFINITY) ? 0.0f : -m_new * c.scale_log2;
     }
+}
+
+// The row's first tile: the reference max is set from it without a rescale (O and l are still 0).
+// Same state as lazy_raise from m = -inf.
+template <int D>
+__device__ __forceinline__ void first_max(WaveState<D> &st, float lmax, float &nbias, const RowCtx &c) {
+    const float m = fmaxf(-INFINITY, pair_max(lmax));  // -inf when the tile is all masked (or NaN)
+    st.m_run = m;
+    st.thr = m + c.lazy_raw;
+    nbias = (m == -INFINITY) ? 0.0f : -m * c.scale_log2;
 }
 
 // max of the lane's 16 scores
@@ -747,7 +757,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         };
 
         int i = 0;
-        f32x16 sa = f32x16{}, sb = f32x16{};
+        f32x16 sa, sb;  // S(e) and S(e + 1), formed before use
         float nbias = 0.0f;
         if (n > 0) {
             // prologue: K(0), V(0) (unless already in flight), K(1); then the list's valid counts;
@@ -770,7 +780,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             resolve_next();  // the prologue barrier
             sa = qk_tile<D>(st, kb0, ctx);
             if (needs_mask(t0, v0, ctx)) apply_mask(sa, t0, v0, ctx);
-            lazy_raise<D>(st, lane_max(sa), nbias, ctx);
+            first_max<D>(st, lane_max(sa), nbias, ctx);
             // steady state, unrolled by two so that every buffer and score register has a fixed
             // role: step e: wait + barrier; K(e+2) -> free K buffer, V(e+1) -> free V buffer; compute
             int t_a = t1, v_a = v1;  // entry i + 1
