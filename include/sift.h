@@ -217,8 +217,8 @@ sift_status sift_sparse_prefill(const sift_layout *layout, const void *d_plan,
  * in the workspace (each workgroup counts its q head's rows in closed form and lists its share of
  * them) while its other workgroups write V^T, and the attention kernel then reads that CSR.
  * Layouts past the single-launch decode's bounds (more than 2048 tiles, 512 documents or 64 tiles
- * in a document, or more than 8192 LA words) run the V^T transpose and the two-launch decode
- * first instead.
+ * in a document; more than 8192 LA words or 2048 CA words in all, or 4096 LA words in one q
+ * head's vectors) run the V^T transpose and the two-launch decode first instead.
  * d_la, d_ca: the layer's bits as for sift_decode_bits.  Other arguments, the output and the
  * 16-byte alignment rule as for sift_sparse_prefill; the result is bit-identical to
  * sift_decode_bits followed by sift_sparse_prefill on the same bits.

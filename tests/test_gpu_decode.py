@@ -109,6 +109,7 @@ def test_decode_empty_layout():
     ("docs_past_bound", [260, 260], [1] * 520, [64, 1], 1),  # 520 documents
     ("doc_tiles_past_bound", [2], [65, 3], [10], 1),        # a 65-tile document
     ("words_past_bound", [16], [64] * 16, [64], 8),         # 8320 LA words
+    ("ca_words_past_bound", [300], [1] * 300, [64], 8),     # 2400 CA words (LA words 2400)
 ])
 def test_decode_single_launch_bounds(name, req_num_docs, doc_tiles, question_len, hq):
     doc_len = [64 * t - (i % 7) for i, t in enumerate(doc_tiles)]

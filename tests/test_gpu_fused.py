@@ -72,6 +72,28 @@ def test_fused_long_documents_multiword_rows():
     assert_close(out[toks, heads], ref, "long docs")
 
 
+@pytest.mark.parametrize("name,req_num_docs,doc_tiles,question_len,hq", [
+    ("at_bounds", [512], [4] * 512, [0], 1),             # G 2048, 512 documents: the single launch
+    ("ca_words_past_bound", [300], [1] * 300, [64], 8),  # 2400 CA words: transpose + two launches
+])
+def test_fused_at_and_past_the_single_launch_bounds(name, req_num_docs, doc_tiles, question_len, hq):
+    """The fused call's decode at the single-launch decode's limits (its workgroups then share the
+    launch with the V^T transpose) and just past one of them: equal to the CSR path, and sampled
+    rows match the oracle."""
+    doc_len = [64 * t - (i % 7) for i, t in enumerate(doc_tiles)]
+    r = len(req_num_docs)
+    case = W.make_case(name, 12, req_num_docs, doc_len, question_len, hq, 1, 64,
+                       np.full((r, hq), 0.3), np.full((r, hq), 0.2))
+    print(f"fused {name}: G={case.q.shape[0] // 64} docs={len(doc_len)}", flush=True)
+    out, _ = _same_as_csr_path(case)
+    rng = np.random.default_rng(7)
+    valid = np.where(valid_tokens(case))[0]
+    toks = np.concatenate([rng.choice(valid, 300), valid[-64:]]).astype(np.int64)
+    heads = rng.integers(0, case.num_q_heads, size=toks.size).astype(np.int32)
+    ref, _ = oracle.attention(case, heads=heads, tokens=toks)
+    assert_close(out[toks, heads], ref, name)
+
+
 def test_fused_long_document():
     """A document of 2,000 tiles (its decode takes the two-launch path): the fused call equals the
     CSR path, and sampled rows match the oracle."""
