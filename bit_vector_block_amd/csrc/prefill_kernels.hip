@@ -28,7 +28,8 @@
 //  * one pipeline step issues all operand reads of the step first, then the
 //    score MFMAs of the next tile interleaved (pinned with scheduling
 //    barriers) with the exponentials of the current tile, then the output
-//    MFMAs of the current tile interleaved with the max tree of the next;
+//    MFMAs of the current tile interleaved with the max tree of the next; the
+//    VALU work left after the last MFMA runs at a raised wave priority;
 //  * exp2 with log2(e) folded into the scale; the running maximum is raised
 //    (and O, l rescaled) only when a tile's maximum exceeds it by more than
 //    kLazyLog2 in log2 units, which bounds P by 2^kLazyLog2 and leaves
